@@ -1,0 +1,301 @@
+"""gzip-guided block-sparse causal attention for AMD MI355X (gfx950).
+
+Thin ctypes binding over libgsa.so (see include/gsa.h).  The names mirror the C ABI:
+``gsa_prepare`` (host gzip stage), ``gsa_build_mask`` (HIP mask kernel),
+``gsa_attn_fwd`` / ``gsa_attn_bwd`` (HIP attention kernels).  torch supplies device
+memory and the current stream; every step of the computation runs in the library.
+If the library has not been built this module raises on first use: there is no
+fallback implementation.
+
+Method: "Gzip-guided Sparse Attention：用压缩率选择长程内容" (daiwk.github.io reproduction
+of arXiv 2607.21752), sections 背景与主要改动 and 核心公式.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch  # loaded first: libgsa binds to the HIP runtime torch has already mapped
+
+__all__ = [
+    "GsaError", "GsaMask", "lib_path", "load_library", "gsa_prepare", "gsa_mask_sizes", "gsa_build_mask",
+    "gsa_attn_fwd", "gsa_attn_bwd", "attention", "zlib_version", "default_head_counts",
+    "GSA_OK", "GSA_ERR_ARG", "GSA_ERR_SHAPE", "GSA_ERR_ZLIB", "GSA_ERR_HIP", "GSA_ERR_UNSUPPORTED",
+]
+
+GSA_OK, GSA_ERR_ARG, GSA_ERR_SHAPE, GSA_ERR_ZLIB, GSA_ERR_HIP, GSA_ERR_UNSUPPORTED = range(6)
+GSA_F32, GSA_BF16 = 0, 1
+GSA_MAX_BLOCKS = 1024
+MASK_FIELDS = ("flags", "n_literal", "row_ptr", "col_idx", "col_ptr", "row_idx", "n_edges",
+               "work_row", "work_col")
+_MASK_DTYPES = (torch.uint8, torch.int32, torch.int32, torch.int32, torch.int32, torch.int32,
+                torch.int64, torch.int32, torch.int32)
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG_DIR, "libgsa.so")
+
+
+class GsaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {_status_name(status)}: {detail}")
+
+
+class _Mask(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("n_blocks", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32 * 3)] + [(f, ctypes.c_void_p) for f in MASK_FIELDS]
+
+
+class _FwdArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("batch", ctypes.c_int64), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int64),
+                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class _BwdArgs(ctypes.Structure):
+    _fields_ = [("f", _FwdArgs), ("dout", ctypes.c_void_p), ("dq", ctypes.c_void_p),
+                ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p), ("workspace", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def load_library():
+    """Loads libgsa.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    i32, i64, vp, cp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_char_p
+    lib.gsa_status_str.argtypes, lib.gsa_status_str.restype = [i32], cp
+    lib.gsa_last_error.argtypes, lib.gsa_last_error.restype = [], cp
+    lib.gsa_zlib_version.argtypes, lib.gsa_zlib_version.restype = [], cp
+    lib.gsa_abi_version.argtypes, lib.gsa_abi_version.restype = [], i32
+    lib.gsa_prepare.argtypes = [vp, i64, i64, i32, i32, vp]
+    lib.gsa_prepare.restype = i32
+    lib.gsa_mask_sizes.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
+    lib.gsa_mask_sizes.restype = i32
+    lib.gsa_build_mask.argtypes = [vp, ctypes.POINTER(_Mask), vp]
+    lib.gsa_build_mask.restype = i32
+    lib.gsa_attn_fwd.argtypes = [ctypes.POINTER(_FwdArgs), ctypes.POINTER(_Mask), vp]
+    lib.gsa_attn_fwd.restype = i32
+    lib.gsa_attn_bwd.argtypes = [ctypes.POINTER(_BwdArgs), ctypes.POINTER(_Mask), vp]
+    lib.gsa_attn_bwd.restype = i32
+    _LIB = lib
+    return lib
+
+
+def _status_name(st: int) -> str:
+    try:
+        return load_library().gsa_status_str(st).decode()
+    except Exception:  # pragma: no cover - only while reporting a load failure
+        return str(st)
+
+
+def _check(st: int, where: str):
+    if st != GSA_OK:
+        raise GsaError(st, where, load_library().gsa_last_error().decode())
+
+
+def zlib_version() -> str:
+    return load_library().gsa_zlib_version().decode()
+
+
+def default_head_counts(heads: int):
+    """Half local, a quarter literal, the rest hybrid ([note] 背景与主要改动)."""
+    return (heads // 2, heads // 4, heads - heads // 2 - heads // 4)
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+# ---------------------------------------------------------------------------------- (1)
+def gsa_prepare(data, block: int, n_threads: int = 0) -> np.ndarray:
+    """Per-block gzip level-1 sizes c [B, N] int32 of host bytes ``data`` uint8 [B, T]."""
+    if isinstance(data, torch.Tensor):
+        if data.device.type != "cpu":
+            raise ValueError("gsa_prepare takes host bytes")
+        data = data.numpy()
+    arr = np.ascontiguousarray(np.asarray(data, dtype=np.uint8))
+    if arr.ndim != 2:
+        raise ValueError("data must be [batch, seq_len]")
+    batch, seq_len = arr.shape
+    n = seq_len // block if block > 0 else 0
+    out = np.zeros((batch, n), dtype=np.int32)
+    st = load_library().gsa_prepare(arr.ctypes.data, batch, seq_len, block, n_threads, out.ctypes.data)
+    _check(st, "gsa_prepare")
+    return out
+
+
+# ---------------------------------------------------------------------------------- (2)
+def gsa_mask_sizes(batch: int, n_blocks: int, n_heads) -> list:
+    nh = (ctypes.c_int32 * 3)(*n_heads)
+    sizes = (ctypes.c_size_t * 9)()
+    _check(load_library().gsa_mask_sizes(batch, n_blocks, nh, sizes), "gsa_mask_sizes")
+    return list(sizes)
+
+
+@dataclass
+class GsaMask:
+    """Device-resident mask of one batch (buffers as in include/gsa.h)."""
+    batch: int
+    n_blocks: int
+    window: int
+    n_heads: tuple
+    flags: torch.Tensor
+    n_literal: torch.Tensor
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+    col_ptr: torch.Tensor
+    row_idx: torch.Tensor
+    n_edges: torch.Tensor
+    work_row: torch.Tensor
+    work_col: torch.Tensor
+
+    @property
+    def cap(self) -> int:
+        return self.n_blocks * (self.n_blocks + 1) // 2
+
+    def struct(self) -> _Mask:
+        m = _Mask()
+        m.batch, m.n_blocks, m.window = self.batch, self.n_blocks, self.window
+        m.n_heads[:] = list(self.n_heads)
+        for f in MASK_FIELDS:
+            setattr(m, f, getattr(self, f).data_ptr())
+        return m
+
+    @staticmethod
+    def empty(batch: int, n_blocks: int, window: int, n_heads, device) -> "GsaMask":
+        sizes = gsa_mask_sizes(batch, n_blocks, n_heads)
+        bufs = {}
+        for f, dt, nbytes in zip(MASK_FIELDS, _MASK_DTYPES, sizes):
+            itemsize = torch.empty(0, dtype=dt).element_size()
+            bufs[f] = torch.empty(max(nbytes // itemsize, 1), dtype=dt, device=device)
+        return GsaMask(batch, n_blocks, window, tuple(int(h) for h in n_heads), **bufs)
+
+
+def gsa_build_mask(c, window: int, n_heads, device=None, out: GsaMask | None = None) -> GsaMask:
+    """Literal flags, CSR/CSC block lists and work order from sizes ``c`` [B, N].
+
+    ``c`` may be a host array (uploaded on the current stream) or a device int32 tensor.
+    """
+    if not isinstance(c, torch.Tensor):
+        c = torch.from_numpy(np.ascontiguousarray(np.asarray(c, dtype=np.int32)))
+    if device is None:
+        device = c.device if c.is_cuda else torch.device("cuda", torch.cuda.current_device())
+    c = c.to(device=device, dtype=torch.int32, non_blocking=True).contiguous()
+    if c.dim() != 2:
+        raise ValueError("c must be [batch, n_blocks]")
+    batch, n = c.shape
+    m = out if out is not None else GsaMask.empty(batch, n, window, n_heads, device)
+    if (m.batch, m.n_blocks) != (batch, n):
+        raise ValueError("preallocated mask has another shape")
+    m.window = window
+    ms = m.struct()
+    _check(load_library().gsa_build_mask(c.data_ptr(), ctypes.byref(ms), _stream_ptr(device)),
+           "gsa_build_mask")
+    return m
+
+
+# ---------------------------------------------------------------------------------- (3), (4)
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GSA_BF16
+    if t.dtype == torch.float32:
+        return GSA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _check_tensors(*ts):
+    ref = ts[0]
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError("tensors must live on the same GPU")
+        if t.dtype != ref.dtype or t.shape != ref.shape:
+            raise ValueError("q, k, v (and o, dout) must share dtype and shape [B, H, T, d]")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if ref.dim() != 4:
+        raise ValueError("tensors must be [B, H, T, d]")
+
+
+def _fwd_struct(q, k, v, o, lse, block, scale) -> _FwdArgs:
+    a = _FwdArgs()
+    a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)
+    a.dtype = _dtype_code(q)
+    a.batch, a.heads, a.seq_len, a.head_dim = q.shape
+    a.block, a.scale = block, float(scale)
+    return a
+
+
+def gsa_attn_fwd(q, k, v, mask: GsaMask, block: int, scale: float = 0.0, with_lse: bool = True,
+                 out=None, lse=None):
+    """O [B, H, T, d] (and LSE fp32 [B, H, T]) of the gzip-masked causal attention."""
+    _check_tensors(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    a = _fwd_struct(q, k, v, o, lse if with_lse else None, block, scale)
+    ms = mask.struct()
+    _check(load_library().gsa_attn_fwd(ctypes.byref(a), ctypes.byref(ms), _stream_ptr(q.device)),
+           "gsa_attn_fwd")
+    return (o, lse) if with_lse else o
+
+
+def gsa_attn_bwd(q, k, v, o, lse, dout, mask: GsaMask, block: int, scale: float = 0.0,
+                 workspace=None, out=None):
+    """dQ, dK, dV of sum(O * dout)."""
+    _check_tensors(q, k, v, o, dout)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
+    if workspace is None:
+        workspace = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    b = _BwdArgs()
+    b.f = _fwd_struct(q, k, v, o, lse, block, scale)
+    b.dout, b.dq, b.dk, b.dv, b.workspace = _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace)
+    ms = mask.struct()
+    _check(load_library().gsa_attn_bwd(ctypes.byref(b), ctypes.byref(ms), _stream_ptr(q.device)),
+           "gsa_attn_bwd")
+    return dq, dk, dv
+
+
+class _GsaAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, mask, block, scale):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, lse = gsa_attn_fwd(q, k, v, mask, block, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.mask, ctx.block, ctx.scale = mask, block, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = gsa_attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.mask, ctx.block, ctx.scale)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q, k, v, mask: GsaMask, block: int, scale: float = 0.0):
+    """Differentiable gzip-masked attention (forward and backward through libgsa)."""
+    return _GsaAttention.apply(q, k, v, mask, block, scale)
+
+
+def softmax_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,74 @@
+"""Builds libgsa.so in-tree for gfx950 with hipcc.
+
+Device sources (*.hip) are compiled with packed-fp32 instructions disabled; host sources
+(*.cpp) are plain C++17 against the HIP runtime API.  Objects go to ``_build/`` at the
+repository root and the shared library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_PATH = os.path.join(PKG_DIR, "libgsa.so")
+ARCH = "gfx950"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+HIP_SOURCES = ["gsa_mask.hip", "gsa_attn_fwd.hip", "gsa_attn_bwd.hip"]
+CPP_SOURCES = ["gsa_api.cpp", "gsa_prepare.cpp"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-ffast-math", "-fno-finite-math-only"]
+
+
+def _hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found; the HIP library cannot be built")
+    return exe
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compiles every source and links libgsa.so; returns the library path."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cmds = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        cmds.append([hipcc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in CPP_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        cmds.append([hipcc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-c",
+                     os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
+        outs = list(ex.map(_run, cmds))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp, "-lz", "-lpthread"])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,30 @@
+// Internal declarations shared by the C ABI layer and the kernel translation units.
+#pragma once
+
+#include <cstdarg>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+#include "gsa.h"
+
+namespace gsa {
+
+// Records a thread-local failure detail and returns `st`.
+gsa_status fail(gsa_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clears the thread-local failure detail.
+void clear_error();
+// Maps a HIP error after a launch to GSA_ERR_HIP with a detail; GSA_OK otherwise.
+gsa_status check_launch(const char *what);
+
+// Kernel launchers (arguments already validated).
+gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t stream);
+gsa_status launch_attn_fwd(const gsa_fwd_args &a, const gsa_mask &m, hipStream_t stream);
+gsa_status launch_attn_bwd(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream);
+
+// Whether a (dtype, block, head_dim) instance is compiled in.
+bool attn_instance_built(int32_t dtype, int32_t block, int32_t head_dim);
+
+inline int64_t mask_cap(int32_t n) { return (int64_t)n * (n + 1) / 2; }
+
+}  // namespace gsa
