@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the gzip-guided block-sparse attention hot path on one MI355X.
+
+One step = one pass of the device path over one batch: upload the per-block gzip
+sizes, build the mask (flags, CSR/CSC lists, work order), forward, and the three
+backward stages.  The host gzip stage (gsa_prepare) is timed separately on the host.
+
+The workload is 8 samples x 8192 bytes, block 64, window 2, 12 heads (6 local /
+3 literal / 3 hybrid), head_dim 64, bf16, forward + backward, on seeded synthetic
+text-like bytes (the pages' PG-19 runs at 8K bytes are the shape it stands in for).
+
+Prints ONE JSON line.  ``value`` is effective TFLOP/s on kept blocks: algorithmic
+FLOPs (4 b^2 d per kept tile forward, 10 b^2 d backward, diagonal tiles counted whole)
+divided by the step time.  ``roofline`` rates the kernel that takes the most time per
+step against its binding MI355X roof, measured with HIP events inside the timed region;
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s on kept blocks + fwd/bwd ms per batch at 8K bytes, % MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNELS = ("mask", "fwd", "bwd_prep", "bwd_dkdv", "bwd_dq")
+KERNEL_SOURCES = {"fwd": "gsa_attn_fwd.hip", "bwd_prep": "gsa_attn_bwd.hip", "bwd_dkdv": "gsa_attn_bwd.hip",
+                  "bwd_dq": "gsa_attn_bwd.hip", "mask": "gsa_mask.hip"}
+
+
+def kernel_source_hash(name: str) -> str:
+    """Hash of the sources a kernel is built from (its file plus the shared headers)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "content_adaptive_block_amd", "csrc")
+    for f in (KERNEL_SOURCES[name], "gsa_attn_common.hpp", "gsa_device.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kept_tiles(n_edges: np.ndarray, n_heads) -> int:
+    """Sum over samples and classes of heads-in-class x kept block pairs."""
+    return int(sum(int(n_heads[k]) * int(n_edges[s, k]) for s in range(n_edges.shape[0]) for k in range(3)))
+
+
+def token_edges(n_edges: np.ndarray, n_heads, n: int, b: int) -> int:
+    """Kept (query, key) token pairs: full b x b off-diagonal tiles plus causal diagonals."""
+    tot = 0
+    for s in range(n_edges.shape[0]):
+        for k in range(3):
+            e = int(n_edges[s, k])
+            tot += int(n_heads[k]) * (b * b * (e - n) + n * b * (b + 1) // 2)
+    return tot
+
+
+def kernel_work(name, wl, tiles):
+    """(algorithmic bytes, algorithmic flops) of one launch of kernel ``name``."""
+    b, d = wl.block, wl.head_dim
+    elem = 4 if wl.dtype == "f32" else 2
+    x = wl.batch * wl.heads * wl.seq_len * d * elem          # one [B, H, T, d] tensor
+    r = wl.batch * wl.heads * wl.seq_len * 4                 # one fp32 [B, H, T] vector
+    tile = b * b * d
+    if name == "fwd":              # read Q K V, write O and LSE
+        return 4 * x + r, 4 * tile * tiles
+    if name == "bwd_prep":         # read O dO, write D
+        return 2 * x + r, 2 * wl.batch * wl.heads * wl.seq_len * d
+    if name == "bwd_dkdv":         # read Q K V dO LSE D, write dK dV; S, dP, dV, dK
+        return 6 * x + 2 * r, 8 * tile * tiles
+    if name == "bwd_dq":           # read Q K V dO LSE D, write dQ; S, dP, dQ
+        return 5 * x + 2 * r, 6 * tile * tiles
+    n = wl.n_blocks
+    return wl.batch * n * 4 * 2 + 3 * wl.batch * (2 * (n + 1) + n * (n + 1)) * 4, 0   # mask
+
+
+def load_traffic(name: str, wl) -> float | None:
+    """Measured HBM bytes per launch from a committed rocprofv3 PMC summary, if that summary
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(name):
+        return None
+    return float(rec["bytes_per_launch"])
+
+
+def cpu_baseline(wl, x_bytes, tensors, masks_np, budget_s: float):
+    """The fp64 oracle on whole heads of sample 0 until ``budget_s`` seconds are spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    c = oracle.compressed_lengths(x_bytes[:1], wl.block)
+    flags, _ = oracle.literal_flags(c, wl.block)
+    bm = oracle.block_masks(flags, wl.window)
+    t_mask = time.perf_counter() - t0
+    classes = oracle.head_classes(wl.n_heads)
+    f64 = lambda z: z.float().numpy().astype(np.float64)
+    done, flops, t_attn = 0, 0.0, 0.0
+    tile = wl.block * wl.block * wl.head_dim
+    for h in range(wl.heads):
+        q, k, v, do = (f64(tensors[nm][0:1, h:h + 1]) for nm in ("q", "k", "v", "do"))
+        nh = [0, 0, 0]
+        nh[classes[h]] = 1
+        sub = np.zeros((1, 3) + bm.shape[2:], dtype=bool)
+        sub[0, classes[h]] = bm[0, classes[h]]
+        t1 = time.perf_counter()
+        oracle.attn_fwd(q, k, v, sub, tuple(nh), wl.block)
+        if wl.backward:
+            oracle.attn_bwd(q, k, v, do, sub, tuple(nh), wl.block)
+        t_attn += time.perf_counter() - t1
+        flops += (14 if wl.backward else 4) * tile * int(bm[0, classes[h]].sum())
+        done += 1
+        if t_attn + t_mask >= budget_s:
+            break
+    secs = t_attn + t_mask
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"sample 0 of {wl.batch}, {done} of {wl.heads} heads, full {wl.seq_len}-byte context; "
+                      f"zlib+mask {t_mask:.2f} s, attention fwd{'+bwd' if wl.backward else ''} {t_attn:.2f} s",
+            "seconds": secs}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="workload id (1-5); 4 is the headline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0: skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(samples shard across GPUs with no communication; run --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import content_adaptive_block_amd as gsa
+    import synth
+
+    wl = synth.WORKLOADS[args.config]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    x = synth.gen_bytes(wl)
+    names = ("q", "k", "v", "do") if wl.backward else ("q", "k", "v")
+    host_t = synth.gen_tensors(wl, names)
+    t = {nm: v.to(dev) for nm, v in host_t.items()}
+
+    # host stage, timed on its own (all cores, then one thread)
+    c = gsa.gsa_prepare(x, wl.block)
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        gsa.gsa_prepare(x, wl.block)
+    prep_ms = (time.perf_counter() - t0) / reps * 1e3
+    t0 = time.perf_counter()
+    for _ in range(3):
+        gsa.gsa_prepare(x, wl.block, n_threads=1)
+    prep1_ms = (time.perf_counter() - t0) / 3 * 1e3
+
+    c_host = torch.from_numpy(c).pin_memory()
+    c_dev = torch.empty_like(c_host, device=dev)
+    mask = gsa.GsaMask.empty(wl.batch, wl.n_blocks, wl.window, wl.n_heads, dev)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(t["q"]) for _ in range(3))
+    ws = torch.empty_like(lse)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        c_dev.copy_(c_host, non_blocking=True)
+        gsa.gsa_build_mask(c_dev, wl.window, wl.n_heads, out=mask)
+        mark(1)
+        gsa.gsa_attn_fwd(t["q"], t["k"], t["v"], mask, wl.block, out=o, lse=lse)
+        mark(2)
+        if wl.backward:
+            for i, stage in enumerate(("prep", "dkdv", "dq")):
+                gsa.gsa_attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], mask, wl.block, workspace=ws,
+                                 out=grads, stage=stage)
+                mark(3 + i)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_ev = 6 if wl.backward else 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    per = {nm: [] for nm in KERNELS[:n_ev - 1]}
+    for ev in evs:
+        for i, nm in enumerate(KERNELS[:n_ev - 1]):
+            per[nm].append(ev[i].elapsed_time(ev[i + 1]))
+    kern_ms = {nm: float(np.mean(v)) for nm, v in per.items()}
+
+    n_edges = mask.n_edges.cpu().numpy().reshape(wl.batch, 3)
+    n_lit = mask.n_literal.cpu().numpy()[:wl.batch]
+    tiles = kept_tiles(n_edges, wl.n_heads)
+    tok = token_edges(n_edges, wl.n_heads, wl.n_blocks, wl.block)
+    tile = wl.block * wl.block * wl.head_dim
+    fl_fwd, fl_bwd = 4 * tile * tiles, (10 * tile * tiles if wl.backward else 0)
+    flops = fl_fwd + fl_bwd
+    value = flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+    fwd_ms = kern_ms["fwd"]
+    bwd_ms = sum(kern_ms.get(nm, 0.0) for nm in ("bwd_prep", "bwd_dkdv", "bwd_dq"))
+
+    kernels = {}
+    for nm, ms in kern_ms.items():
+        nbytes, nflops = kernel_work(nm, wl, tiles)
+        kernels[nm] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                       "TFLOP/s": round(nflops / (ms * 1e-3) / 1e12, 2), "bytes": nbytes, "flops": nflops}
+    dom = max((nm for nm in kern_ms if nm != "mask"), key=lambda nm: kern_ms[nm])
+    nbytes, nflops = kernel_work(dom, wl, tiles)
+    t_hbm, t_mfma = nbytes / (PEAK_HBM_GBS * 1e9), nflops / (peak * 1e12)
+    sec = kern_ms[dom] * 1e-3
+    traffic = load_traffic(dom, wl)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(nflops / sec / 1e12, 2), "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = nflops
+
+    rec = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.batch} x {wl.seq_len} bytes, block {wl.block}, window {wl.window}, "
+                               f"{wl.heads} heads {'/'.join(map(str, wl.n_heads))}, head_dim {wl.head_dim}, "
+                               f"{wl.dtype}, {'fwd+bwd' if wl.backward else 'fwd'}",
+                   "global_batch": wl.batch, "seq_len": wl.seq_len, "parallelism": "single GPU"},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "mask_ms": round(kern_ms["mask"], 4),
+        "pct_mfma_peak": round(100 * value / peak, 2),
+        "token_exact_tflops": round((4 + (10 if wl.backward else 0)) * wl.head_dim * tok / (ms_step * 1e-3) / 1e12, 3),
+        "kept_tiles": tiles, "literal_blocks": n_lit.tolist(),
+        "host_prepare_ms": {"all_cores": round(prep_ms, 3), "one_thread": round(prep1_ms, 3)},
+        "kernels": kernels, "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        rec["cpu_baseline"] = cpu_baseline(wl, x, host_t, None, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -90,8 +90,10 @@ def load_library():
     lib.gsa_build_mask.restype = i32
     lib.gsa_attn_fwd.argtypes = [ctypes.POINTER(_FwdArgs), ctypes.POINTER(_Mask), vp]
     lib.gsa_attn_fwd.restype = i32
-    lib.gsa_attn_bwd.argtypes = [ctypes.POINTER(_BwdArgs), ctypes.POINTER(_Mask), vp]
-    lib.gsa_attn_bwd.restype = i32
+    for nm in ("gsa_attn_bwd", "gsa_attn_bwd_prep", "gsa_attn_bwd_dkdv", "gsa_attn_bwd_dq"):
+        fn = getattr(lib, nm)
+        fn.argtypes = [ctypes.POINTER(_BwdArgs), ctypes.POINTER(_Mask), vp]
+        fn.restype = i32
     _LIB = lib
     return lib
 
@@ -260,19 +262,29 @@ def gsa_attn_fwd(q, k, v, mask: GsaMask, block: int, scale: float = 0.0, with_ls
     return (o, lse) if with_lse else o
 
 
+def _bwd_struct(q, k, v, o, lse, dout, dq, dk, dv, workspace, block, scale) -> _BwdArgs:
+    b = _BwdArgs()
+    b.f = _fwd_struct(q, k, v, o, lse, block, scale)
+    b.dout, b.dq, b.dk, b.dv, b.workspace = _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace)
+    return b
+
+
+BWD_STAGES = {"all": "gsa_attn_bwd", "prep": "gsa_attn_bwd_prep", "dkdv": "gsa_attn_bwd_dkdv",
+              "dq": "gsa_attn_bwd_dq"}
+
+
 def gsa_attn_bwd(q, k, v, o, lse, dout, mask: GsaMask, block: int, scale: float = 0.0,
-                 workspace=None, out=None):
-    """dQ, dK, dV of sum(O * dout)."""
+                 workspace=None, out=None, stage: str = "all"):
+    """dQ, dK, dV of sum(O * dout).  ``stage`` runs one backward stage only
+    ("prep", "dkdv" or "dq", in that order, sharing ``workspace`` and ``out``)."""
     _check_tensors(q, k, v, o, dout)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
     if workspace is None:
         workspace = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    b = _BwdArgs()
-    b.f = _fwd_struct(q, k, v, o, lse, block, scale)
-    b.dout, b.dq, b.dk, b.dv, b.workspace = _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace)
+    b = _bwd_struct(q, k, v, o, lse, dout, dq, dk, dv, workspace, block, scale)
     ms = mask.struct()
-    _check(load_library().gsa_attn_bwd(ctypes.byref(b), ctypes.byref(ms), _stream_ptr(q.device)),
-           "gsa_attn_bwd")
+    fn = getattr(load_library(), BWD_STAGES[stage])
+    _check(fn(ctypes.byref(b), ctypes.byref(ms), _stream_ptr(q.device)), BWD_STAGES[stage])
     return dq, dk, dv
 
 

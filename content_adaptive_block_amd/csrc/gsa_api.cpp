@@ -141,7 +141,7 @@ gsa_status gsa_attn_fwd(const gsa_fwd_args *a, const gsa_mask *m, hipStream_t st
   return launch_attn_fwd(*a, *m, stream);
 }
 
-gsa_status gsa_attn_bwd(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream) {
+static gsa_status attn_bwd_stages(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream, int stages) {
   clear_error();
   if (!a) return fail(GSA_ERR_ARG, "args is NULL");
   gsa_status st = check_fwd(&a->f, m);
@@ -152,7 +152,23 @@ gsa_status gsa_attn_bwd(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t st
   if (!aligned16(a->dout) || !aligned16(a->dq) || !aligned16(a->dk) || !aligned16(a->dv) ||
       !aligned16(a->workspace))
     return fail(GSA_ERR_ARG, "dout/dq/dk/dv/workspace must be 16-byte aligned");
-  return launch_attn_bwd(*a, *m, stream);
+  return launch_attn_bwd(*a, *m, stream, stages);
+}
+
+gsa_status gsa_attn_bwd(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream) {
+  return attn_bwd_stages(a, m, stream, kBwdAll);
+}
+
+gsa_status gsa_attn_bwd_prep(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream) {
+  return attn_bwd_stages(a, m, stream, kBwdPrep);
+}
+
+gsa_status gsa_attn_bwd_dkdv(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream) {
+  return attn_bwd_stages(a, m, stream, kBwdDkdv);
+}
+
+gsa_status gsa_attn_bwd_dq(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream) {
+  return attn_bwd_stages(a, m, stream, kBwdDq);
 }
 
 }  // extern "C"

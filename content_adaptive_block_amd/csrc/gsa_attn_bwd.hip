@@ -211,7 +211,7 @@ __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dq_kernel(
 }
 
 template <typename T, int BLK, int HD>
-gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream) {
+gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream, int stages) {
   using S = AttnShape<T, BLK, HD>;
   const gsa_fwd_args &f = a.f;
   const int64_t items = f.batch * f.heads * (int64_t)m.n_blocks;
@@ -225,36 +225,42 @@ gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStre
   const T *dout = static_cast<const T *>(a.dout);
 
   constexpr int kLanes = HD / (16 / sizeof(T));
-  const int64_t pre_threads = rows * kLanes;
-  hipLaunchKernelGGL((bwd_pre_kernel<T, HD>), dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0,
-                     stream, o, dout, a.workspace, rows);
-  gsa_status st = check_launch("bwd_pre_kernel");
-  if (st != GSA_OK) return st;
-
+  if (stages & kBwdPrep) {
+    const int64_t pre_threads = rows * kLanes;
+    hipLaunchKernelGGL((bwd_pre_kernel<T, HD>), dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0,
+                       stream, o, dout, a.workspace, rows);
+    gsa_status st = check_launch("bwd_pre_kernel");
+    if (st != GSA_OK) return st;
+  }
   const unsigned grid = (unsigned)padded_grid(items);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, BLK, HD>), dim3(grid), dim3(S::kThreads), 0, stream, q, k, v, dout,
-                     f.lse, a.workspace, static_cast<T *>(a.dk), static_cast<T *>(a.dv), m.col_ptr, m.row_idx,
-                     m.work_col, f.heads, m.n_blocks, mask_cap(m.n_blocks), m.n_heads[0], m.n_heads[1], items,
-                     sl2, scale);
-  st = check_launch("bwd_dkdv_kernel");
-  if (st != GSA_OK) return st;
-
-  hipLaunchKernelGGL((bwd_dq_kernel<T, BLK, HD>), dim3(grid), dim3(S::kThreads), 0, stream, q, k, v, dout,
-                     f.lse, a.workspace, static_cast<T *>(a.dq), m.row_ptr, m.col_idx, m.work_row, f.heads,
-                     m.n_blocks, mask_cap(m.n_blocks), m.n_heads[0], m.n_heads[1], items, sl2, scale);
-  return check_launch("bwd_dq_kernel");
+  if (stages & kBwdDkdv) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, BLK, HD>), dim3(grid), dim3(S::kThreads), 0, stream, q, k, v, dout,
+                       f.lse, a.workspace, static_cast<T *>(a.dk), static_cast<T *>(a.dv), m.col_ptr, m.row_idx,
+                       m.work_col, f.heads, m.n_blocks, mask_cap(m.n_blocks), m.n_heads[0], m.n_heads[1], items,
+                       sl2, scale);
+    gsa_status st = check_launch("bwd_dkdv_kernel");
+    if (st != GSA_OK) return st;
+  }
+  if (stages & kBwdDq) {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, BLK, HD>), dim3(grid), dim3(S::kThreads), 0, stream, q, k, v, dout,
+                       f.lse, a.workspace, static_cast<T *>(a.dq), m.row_ptr, m.col_idx, m.work_row, f.heads,
+                       m.n_blocks, mask_cap(m.n_blocks), m.n_heads[0], m.n_heads[1], items, sl2, scale);
+    gsa_status st = check_launch("bwd_dq_kernel");
+    if (st != GSA_OK) return st;
+  }
+  return GSA_OK;
 }
 
 }  // namespace
 
-gsa_status launch_attn_bwd(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream) {
+gsa_status launch_attn_bwd(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream, int stages) {
   const gsa_fwd_args &f = a.f;
   if (f.dtype == GSA_F32 && f.block == 16 && f.head_dim == 32)
-    return launch_bwd_instance<float, 16, 32>(a, m, stream);
+    return launch_bwd_instance<float, 16, 32>(a, m, stream, stages);
   if (f.dtype == GSA_BF16 && f.block == 64 && f.head_dim == 64)
-    return launch_bwd_instance<bf16_t, 64, 64>(a, m, stream);
+    return launch_bwd_instance<bf16_t, 64, 64>(a, m, stream, stages);
   if (f.dtype == GSA_BF16 && f.block == 128 && f.head_dim == 128)
-    return launch_bwd_instance<bf16_t, 128, 128>(a, m, stream);
+    return launch_bwd_instance<bf16_t, 128, 128>(a, m, stream, stages);
   return fail(GSA_ERR_UNSUPPORTED, "no backward kernel for dtype %d, block %d, head_dim %d", f.dtype, f.block,
               f.head_dim);
 }

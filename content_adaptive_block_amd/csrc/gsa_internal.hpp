@@ -20,7 +20,9 @@ gsa_status check_launch(const char *what);
 // Kernel launchers (arguments already validated).
 gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t stream);
 gsa_status launch_attn_fwd(const gsa_fwd_args &a, const gsa_mask &m, hipStream_t stream);
-gsa_status launch_attn_bwd(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream);
+// Backward stages: bit 0 = D precompute, bit 1 = dK/dV, bit 2 = dQ (run in that order).
+enum : int { kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7 };
+gsa_status launch_attn_bwd(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream, int stages);
 
 // Whether a (dtype, block, head_dim) instance is compiled in.
 bool attn_instance_built(int32_t dtype, int32_t block, int32_t head_dim);

@@ -190,6 +190,16 @@ typedef struct {
 
 gsa_status gsa_attn_bwd(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream);
 
+/* The three stages gsa_attn_bwd enqueues, in its order, for callers that time or
+ * schedule them separately (same arguments, validation and errors as gsa_attn_bwd):
+ *   gsa_attn_bwd_prep  D_t = sum_f dO_tf O_tf into a->workspace;
+ *   gsa_attn_bwd_dkdv  dK, dV over the CSC column lists (reads D);
+ *   gsa_attn_bwd_dq    dQ over the CSR row lists (reads D).
+ * dkdv and dq are independent of each other once prep has run. */
+gsa_status gsa_attn_bwd_prep(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream);
+gsa_status gsa_attn_bwd_dkdv(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream);
+gsa_status gsa_attn_bwd_dq(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
