@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5); 4 is the headline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0: skip)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB 5 times (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -158,6 +160,14 @@ def main():
     wl = synth.WORKLOADS[args.config]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4}))
+        return
 
     x = synth.gen_bytes(wl)
     names = ("q", "k", "v", "do") if wl.backward else ("q", "k", "v")

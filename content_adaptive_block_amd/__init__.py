@@ -30,9 +30,9 @@ GSA_OK, GSA_ERR_ARG, GSA_ERR_SHAPE, GSA_ERR_ZLIB, GSA_ERR_HIP, GSA_ERR_UNSUPPORT
 GSA_F32, GSA_BF16 = 0, 1
 GSA_MAX_BLOCKS = 1024
 MASK_FIELDS = ("flags", "n_literal", "row_ptr", "col_idx", "col_ptr", "row_idx", "n_edges",
-               "work_row", "work_col")
+               "work_row", "work_col", "sched")
 _MASK_DTYPES = (torch.uint8, torch.int32, torch.int32, torch.int32, torch.int32, torch.int32,
-                torch.int64, torch.int32, torch.int32)
+                torch.int64, torch.int32, torch.int32, torch.int32)
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 
@@ -148,7 +148,7 @@ def gsa_prepare(data, block: int, n_threads: int = 0) -> np.ndarray:
 # ---------------------------------------------------------------------------------- (2)
 def gsa_mask_sizes(batch: int, n_blocks: int, n_heads) -> list:
     nh = (ctypes.c_int32 * 3)(*n_heads)
-    sizes = (ctypes.c_size_t * 9)()
+    sizes = (ctypes.c_size_t * 10)()
     _check(load_library().gsa_mask_sizes(batch, n_blocks, nh, sizes), "gsa_mask_sizes")
     return list(sizes)
 
@@ -169,6 +169,7 @@ class GsaMask:
     n_edges: torch.Tensor
     work_row: torch.Tensor
     work_col: torch.Tensor
+    sched: torch.Tensor
 
     @property
     def cap(self) -> int:

@@ -24,8 +24,9 @@ HIP_SOURCES = ["gsa_mask.hip", "gsa_attn_fwd.hip", "gsa_attn_bwd.hip"]
 CPP_SOURCES = ["gsa_api.cpp", "gsa_prepare.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+# MFMA accumulators stay in ordinary VGPRs (no AGPR copies around every product).
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-ffast-math", "-fno-finite-math-only"]
+          "-ffast-math", "-fno-finite-math-only", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _hipcc() -> str:
@@ -43,15 +44,19 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compiles every source and links libgsa.so; returns the library path."""
+def build(verbose: bool = False, jobs: int = 8, defines=(), out: str | None = None) -> str:
+    """Compiles every source and links libgsa.so (or ``out``); returns the library path.
+
+    ``defines`` are extra preprocessor definitions (NAME or NAME=VALUE) for the device
+    sources, e.g. a different LDS ring depth."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
     cmds = []
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        cmds.append([hipcc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *COMMON, *DEVICE, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CPP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
@@ -64,10 +69,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         for o in outs:
             if o.strip():
                 print(o)
-    tmp = LIB_PATH + ".tmp"
+    target = out or LIB_PATH
+    tmp = target + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp, "-lz", "-lpthread"])
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":

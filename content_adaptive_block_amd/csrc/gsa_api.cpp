@@ -43,6 +43,7 @@ static gsa_status check_mask(const gsa_mask *m, bool need_flags) {
     return fail(GSA_ERR_UNSUPPORTED, "n_blocks %d outside 1..%d", m->n_blocks, GSA_MAX_BLOCKS);
   if (!m->row_ptr || !m->col_idx || !m->col_ptr || !m->row_idx || !m->work_row || !m->work_col)
     return fail(GSA_ERR_ARG, "mask list buffer is NULL");
+  if (!m->sched) return fail(GSA_ERR_ARG, "mask sched buffer is NULL");
   if (need_flags && (!m->flags || !m->n_literal || !m->n_edges))
     return fail(GSA_ERR_ARG, "mask flag/count buffer is NULL");
   int64_t items = m->batch * (int64_t)(m->n_heads[0] + m->n_heads[1] + m->n_heads[2]) * m->n_blocks;
@@ -74,7 +75,7 @@ static gsa_status check_fwd(const gsa_fwd_args *a, const gsa_mask *m) {
   if (!a->q || !a->k || !a->v || !a->o) return fail(GSA_ERR_ARG, "q/k/v/o is NULL");
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
     return fail(GSA_ERR_ARG, "q/k/v/o must be 16-byte aligned");
-  if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return fail(GSA_ERR_ARG, "lse misaligned");
+  if (a->lse && !aligned16(a->lse)) return fail(GSA_ERR_ARG, "lse must be 16-byte aligned");
   return GSA_OK;
 }
 
@@ -121,6 +122,7 @@ gsa_status gsa_mask_sizes(int64_t batch, int32_t n_blocks, const int32_t n_heads
   sizes_out[6] = B * 3 * 8;                  // n_edges
   sizes_out[7] = B * H * N * 4;              // work_row
   sizes_out[8] = B * H * N * 4;              // work_col
+  sizes_out[9] = (size_t)(sched_words(batch, n_blocks) + 8) * 4;  // sched: scratch + long-item counts
   return GSA_OK;
 }
 

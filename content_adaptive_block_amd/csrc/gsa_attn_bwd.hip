@@ -11,11 +11,15 @@
 //   bwd_pre   D for every row (fp32).
 //   bwd_dkdv  one workgroup per (sample, head, kv-block j), walking the CSC column of j
 //             (query blocks i that keep j); each wave keeps 16 keys of K_j, V_j in
-//             registers and accumulates dK^T, dV^T tiles in fp32 while Q_i and dO_i are
-//             staged in LDS (row-major and transposed).
+//             registers and accumulates dK^T, dV^T tiles in fp32 while Q_i, dO_i, LSE_i
+//             and D_i stream through two LDS stages by asynchronous global -> LDS copies
+//             one block ahead; Q_i^T and dO_i^T come from transposing LDS reads.
 //   bwd_dq    one workgroup per (sample, head, query block i), walking the CSR row of i;
 //             each wave keeps 16 query rows of Q_i and dO_i in registers and accumulates
-//             dQ^T while K_j (both layouts) and V_j are staged in LDS.
+//             dQ^T while K_j and V_j stream the same way (K_j^T by transposing reads).
+// Short lists run in packets of neighbouring blocks (see packet_of).
+#include <type_traits>
+
 #include "gsa_attn_common.hpp"
 
 namespace gsa {
@@ -53,161 +57,258 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ o, c
   if (row < rows && part == 0) dvec[row] = acc;
 }
 
+// Packet size: neighbouring blocks share one workgroup when tiles are small.
+template <typename T, int BLK, int HD>
+constexpr int bwd_group() {
+  return AttnShape<T, BLK, HD>::kTileBytes <= 8 * 1024 ? kGroup : 1;
+}
+
+// dK, dV of one (sample, head, kv-block j): walk the query blocks i of column j.
+template <typename T, int BLK, int HD>
+struct DkdvPolicy {
+  using S = AttnShape<T, BLK, HD>;
+  using Item = WorkItem;
+  // A stage holds Q_i, dO_i, then LSE_i and D_i (BLK floats each).
+  static constexpr int kStageBytes = 2 * S::kTileBytes + 2 * BLK * 4;
+  static constexpr int kStores = 2 * S::kDB;
+  // Each wave copies 16 of the BLK floats of LSE_i and of D_i (4-byte copies, 16 lanes).
+  static_assert(BLK == 16 * S::kWaves, "vector slice per wave");
+  // At d = 128 a wave's 256 registers cannot also hold the next item's K/V rows; those
+  // instances run one item per workgroup and load them directly.
+  static constexpr bool kAhead = HD <= 64;
+  struct NoFrag {};
+  using NextFrag = typename std::conditional<kAhead, typename S::QFrag, NoFrag>::type;
+
+  WorkLists wl;
+  const T *q, *k, *v, *dout;
+  const float *lse, *dvec;
+  T *dk, *dv;
+  int64_t seq;
+  float sl2, scale;
+  unsigned char *lds;
+  int tid, c, g, key_in_blk;
+
+  typename S::QFrag kf, vf;
+  NextFrag kn, vn;
+  f32x4 dk_acc[S::kDB], dv_acc[S::kDB];
+
+  __device__ Item decode(int64_t pos) const { return wl.decode(pos); }
+  __device__ void operands(const Item &it) {
+    const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key_in_blk;
+    if constexpr (kAhead) {
+      S::load_row_frag(kn, k + key_row * HD, g);
+      S::load_row_frag(vn, v + key_row * HD, g);
+    } else {
+      S::load_row_frag(kf, k + key_row * HD, g);
+      S::load_row_frag(vf, v + key_row * HD, g);
+    }
+  }
+  __device__ void begin(const Item &) {
+    if constexpr (kAhead) {
+      kf = kn;
+      vf = vn;
+    }
+#pragma unroll
+    for (int db = 0; db < S::kDB; ++db) {
+      dk_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  __device__ void copy(const Item &it, int i, int stage) {
+    const int64_t row0 = it.sh * seq + (int64_t)i * BLK;
+    unsigned char *dst = lds + stage * kStageBytes;
+    S::copy_tile(dst, q + row0 * HD, tid);
+    S::copy_tile(dst + S::kTileBytes, dout + row0 * HD, tid);
+    const int wave = tid >> 6, lane = tid & 63;
+    if (lane < 16) {
+      const int x = wave * 16 + lane;
+      copy4_to_lds(lse + row0 + x, dst + 2 * S::kTileBytes + wave * 64);
+      copy4_to_lds(dvec + row0 + x, dst + 2 * S::kTileBytes + BLK * 4 + wave * 64);
+    }
+  }
+  __device__ void compute(const Item &it, int e, int stage) {
+    const unsigned char *lq = lds + stage * kStageBytes;
+    const unsigned char *ldo = lq + S::kTileBytes;
+    const float *ll = reinterpret_cast<const float *>(lq + 2 * S::kTileBytes);
+    const float *ld = ll + BLK;
+    const bool diag = e == it.beg;   // column j starts with its own block i = j
+    // P[q][key] and dS[q][key], one part of 16*kPartTiles queries at a time;
+    // lane: key c, queries qb*16 + 4g + r.
+#pragma unroll
+    for (int part = 0; part < S::kParts; ++part) {
+      f32x4 p[S::kPartTiles], ds[S::kPartTiles];
+#pragma unroll
+      for (int t = 0; t < S::kPartTiles; ++t) {
+        const int qb = part * S::kPartTiles + t;
+        const f32x4 st = S::dot_rows(lq, qb * 16 + c, g, kf);
+        const f32x4 dp = S::dot_rows(ldo, qb * 16 + c, g, vf);
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ll + qb * 16 + 4 * g);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ld + qb * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float pr = fast_exp2(fmaf(st[r], sl2, -l4[r] * kLog2e));
+          if (diag && key_in_blk > qb * 16 + 4 * g + r) pr = 0.f;
+          p[t][r] = pr;
+          ds[t][r] = pr * (dp[r] - d4[r]);
+        }
+      }
+      S::accumulate_part(dv_acc, ldo, p, part, c, g);
+      S::accumulate_part(dk_acc, lq, ds, part, c, g);
+    }
+  }
+  __device__ void finish(const Item &it) {
+    // Lane holds features db*16 + 4g + r of its key: four consecutive features.
+    const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key_in_blk;
+    T *dkr = dk + key_row * HD;
+    T *dvr = dv + key_row * HD;
+#pragma unroll
+    for (int db = 0; db < S::kDB; ++db) {
+      S::store4(dkr + db * 16 + 4 * g, dk_acc[db] * scale);
+      S::store4(dvr + db * 16 + 4 * g, dv_acc[db]);
+    }
+  }
+};
+
 template <typename T, int BLK, int HD>
 __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ dvec, T *__restrict__ dk, T *__restrict__ dv,
-    const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ row_idx, const int32_t *__restrict__ work,
-    int heads, int n, int64_t cap, int n_loc, int n_lit, int64_t items, float sl2, float scale) {
-  using S = AttnShape<T, BLK, HD>;
-  __shared__ __align__(16) T s_q[BLK * S::kRowStride];
-  __shared__ __align__(16) T s_qt[HD * S::kTStride];
-  __shared__ __align__(16) T s_do[BLK * S::kRowStride];
-  __shared__ __align__(16) T s_dot[HD * S::kTStride];
-  __shared__ float s_lse[BLK];
-  __shared__ float s_d[BLK];
+    WorkLists wl, const int32_t *__restrict__ n_long_ptr, int64_t items, float sl2, float scale) {
+  using P = DkdvPolicy<T, BLK, HD>;
+  constexpr int G = bwd_group<T, BLK, HD>();
+  __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
+  int64_t first;
+  int count;
+  packet_of(blockIdx.x, items, G > 1 ? *n_long_ptr : items, G, &first, &count);
+  if (count == 0) return;
 
-  const int64_t pos = work_position(blockIdx.x, items);
-  if (pos < 0) return;
-  const int64_t item = work[pos];
-  const int j = (int)(item % n);
-  const int64_t sh = item / n;
-  const int h = (int)(sh % heads);
-  const int64_t s = sh / heads;
-  const int cls = head_class(h, n_loc, n_lit);
-  const int32_t *cp = col_ptr + (s * 3 + cls) * (int64_t)(n + 1);
-  const int32_t *ridx = row_idx + (s * 3 + cls) * cap;
-  const int beg = cp[j], end = cp[j + 1];
-
-  const int64_t seq = (int64_t)n * BLK;
-  const int64_t head_off = sh * seq * HD;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const int key_in_blk = wave * 16 + c;
-  const int64_t key_row = (int64_t)j * BLK + key_in_blk;
-
-  typename S::QFrag kf, vf;
-  S::load_row_frag(kf, k + head_off + key_row * HD, g);
-  S::load_row_frag(vf, v + head_off + key_row * HD, g);
-
-  f32x4 dk_acc[S::kDB], dv_acc[S::kDB];
-#pragma unroll
-  for (int db = 0; db < S::kDB; ++db) {
-    dk_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  for (int e = beg; e < end; ++e) {
-    const int i = ridx[e];
-    const int64_t blk_off = head_off + (int64_t)i * BLK * HD;
-    __syncthreads();
-    S::stage_rows(s_q, q + blk_off, tid);
-    S::stage_cols(s_qt, q + blk_off, tid);
-    S::stage_rows(s_do, dout + blk_off, tid);
-    S::stage_cols(s_dot, dout + blk_off, tid);
-    for (int t = tid; t < BLK; t += S::kThreads) {
-      s_lse[t] = lse[sh * seq + (int64_t)i * BLK + t] * kLog2e;
-      s_d[t] = dvec[sh * seq + (int64_t)i * BLK + t];
-    }
-    __syncthreads();
-
-    // P[q][key] and dS[q][key] for the 16-query tiles of block i; lane: key c, queries 4g+r.
-    f32x4 p[S::kKB], ds[S::kKB];
-#pragma unroll
-    for (int qb = 0; qb < S::kKB; ++qb) {
-      const f32x4 st = S::dot_rows(s_q, qb * 16 + c, g, kf);
-      const f32x4 dp = S::dot_rows(s_do, qb * 16 + c, g, vf);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qi = qb * 16 + 4 * g + r;
-        float pr = fast_exp2(fmaf(st[r], sl2, -s_lse[qi]));
-        if (i == j && key_in_blk > qi) pr = 0.f;
-        p[qb][r] = pr;
-        ds[qb][r] = pr * (dp[r] - s_d[qi]);
-      }
-    }
-    S::accumulate_pv(dv_acc, s_dot, p, c, g);
-    S::accumulate_pv(dk_acc, s_qt, ds, c, g);
-  }
-
-  // Lane holds features db*16 + 4g + r of key key_row: four consecutive features.
-  T *dkr = dk + head_off + key_row * HD;
-  T *dvr = dv + head_off + key_row * HD;
-#pragma unroll
-  for (int db = 0; db < S::kDB; ++db) {
-    S::store4(dkr + db * 16 + 4 * g, dk_acc[db] * scale);
-    S::store4(dvr + db * 16 + 4 * g, dv_acc[db]);
-  }
+  P pol;
+  pol.wl = wl;
+  pol.q = q;
+  pol.k = k;
+  pol.v = v;
+  pol.dout = dout;
+  pol.lse = lse;
+  pol.dvec = dvec;
+  pol.dk = dk;
+  pol.dv = dv;
+  pol.seq = (int64_t)wl.n * BLK;
+  pol.sl2 = sl2;
+  pol.scale = scale;
+  pol.lds = lds;
+  pol.tid = threadIdx.x;
+  pol.c = threadIdx.x & 15;
+  pol.g = (threadIdx.x & 63) >> 4;
+  pol.key_in_blk = (threadIdx.x >> 6) * 16 + pol.c;
+  run_packet<G>(pol, first, count);
 }
+
+// dQ of one (sample, head, query block i): walk the kv-blocks j of row i.
+template <typename T, int BLK, int HD>
+struct DqPolicy {
+  using S = AttnShape<T, BLK, HD>;
+  using Item = WorkItem;
+  static constexpr int kStageBytes = 2 * S::kTileBytes;
+  static constexpr int kStores = S::kDB;
+
+  WorkLists wl;
+  const T *q, *k, *v, *dout;
+  const float *lse, *dvec;
+  T *dq;
+  int64_t seq;
+  float sl2, scale;
+  unsigned char *lds;
+  int tid, c, g, q_in_blk;
+
+  typename S::QFrag qf, dof, qn, don;
+  float lse2, dd, lsen, ddn;
+  f32x4 acc[S::kDB];
+
+  __device__ Item decode(int64_t pos) const { return wl.decode(pos); }
+  __device__ void operands(const Item &it) {
+    const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk;
+    S::load_row_frag(qn, q + q_row * HD, g);
+    S::load_row_frag(don, dout + q_row * HD, g);
+    lsen = lse[q_row];
+    ddn = dvec[q_row];
+  }
+  __device__ void begin(const Item &) {
+    qf = qn;
+    dof = don;
+    lse2 = lsen * kLog2e;
+    dd = ddn;
+#pragma unroll
+    for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ void copy(const Item &it, int j, int stage) {
+    const int64_t off = (it.sh * seq + (int64_t)j * BLK) * HD;
+    unsigned char *dst = lds + stage * kStageBytes;
+    S::copy_tile(dst, k + off, tid);
+    S::copy_tile(dst + S::kTileBytes, v + off, tid);
+  }
+  __device__ void compute(const Item &it, int e, int stage) {
+    const unsigned char *lk = lds + stage * kStageBytes;
+    const unsigned char *lv = lk + S::kTileBytes;
+    const bool diag = e == it.end - 1;   // row i ends with its own block j = i
+    // dS^T[key][q], one part of 16*kPartTiles keys at a time: lane holds keys
+    // kb*16 + 4g + r of its query.
+#pragma unroll
+    for (int part = 0; part < S::kParts; ++part) {
+      f32x4 ds[S::kPartTiles];
+#pragma unroll
+      for (int t = 0; t < S::kPartTiles; ++t) {
+        const int kb = part * S::kPartTiles + t;
+        const f32x4 st = S::dot_rows(lk, kb * 16 + c, g, qf);
+        const f32x4 dp = S::dot_rows(lv, kb * 16 + c, g, dof);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float pr = fast_exp2(fmaf(st[r], sl2, -lse2));
+          if (diag && kb * 16 + 4 * g + r > q_in_blk) pr = 0.f;
+          ds[t][r] = pr * (dp[r] - dd);
+        }
+      }
+      S::accumulate_part(acc, lk, ds, part, c, g);
+    }
+  }
+  __device__ void finish(const Item &it) {
+    const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk;
+    T *dqr = dq + q_row * HD;
+#pragma unroll
+    for (int db = 0; db < S::kDB; ++db) S::store4(dqr + db * 16 + 4 * g, acc[db] * scale);
+  }
+};
 
 template <typename T, int BLK, int HD>
 __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dq_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dout,
-    const float *__restrict__ lse, const float *__restrict__ dvec, T *__restrict__ dq,
-    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx, const int32_t *__restrict__ work,
-    int heads, int n, int64_t cap, int n_loc, int n_lit, int64_t items, float sl2, float scale) {
-  using S = AttnShape<T, BLK, HD>;
-  __shared__ __align__(16) T s_k[BLK * S::kRowStride];
-  __shared__ __align__(16) T s_kt[HD * S::kTStride];
-  __shared__ __align__(16) T s_v[BLK * S::kRowStride];
+    const float *__restrict__ lse, const float *__restrict__ dvec, T *__restrict__ dq, WorkLists wl,
+    const int32_t *__restrict__ n_long_ptr, int64_t items, float sl2, float scale) {
+  using P = DqPolicy<T, BLK, HD>;
+  constexpr int G = bwd_group<T, BLK, HD>();
+  __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
+  int64_t first;
+  int count;
+  packet_of(blockIdx.x, items, G > 1 ? *n_long_ptr : items, G, &first, &count);
+  if (count == 0) return;
 
-  const int64_t pos = work_position(blockIdx.x, items);
-  if (pos < 0) return;
-  const int64_t item = work[pos];
-  const int i = (int)(item % n);
-  const int64_t sh = item / n;
-  const int h = (int)(sh % heads);
-  const int64_t s = sh / heads;
-  const int cls = head_class(h, n_loc, n_lit);
-  const int32_t *rp = row_ptr + (s * 3 + cls) * (int64_t)(n + 1);
-  const int32_t *cidx = col_idx + (s * 3 + cls) * cap;
-  const int beg = rp[i], end = rp[i + 1];
-
-  const int64_t seq = (int64_t)n * BLK;
-  const int64_t head_off = sh * seq * HD;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const int q_in_blk = wave * 16 + c;
-  const int64_t q_row = (int64_t)i * BLK + q_in_blk;
-
-  typename S::QFrag qf, dof;
-  S::load_row_frag(qf, q + head_off + q_row * HD, g);
-  S::load_row_frag(dof, dout + head_off + q_row * HD, g);
-  const float lse2 = lse[sh * seq + q_row] * kLog2e;
-  const float dd = dvec[sh * seq + q_row];
-
-  f32x4 acc[S::kDB];
-#pragma unroll
-  for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int e = beg; e < end; ++e) {
-    const int j = cidx[e];
-    const int64_t blk_off = head_off + (int64_t)j * BLK * HD;
-    __syncthreads();
-    S::stage_rows(s_k, k + blk_off, tid);
-    S::stage_cols(s_kt, k + blk_off, tid);
-    S::stage_rows(s_v, v + blk_off, tid);
-    __syncthreads();
-
-    // dS^T[key][q]: lane holds keys kb*16 + 4g + r of its query.
-    f32x4 ds[S::kKB];
-#pragma unroll
-    for (int kb = 0; kb < S::kKB; ++kb) {
-      const f32x4 st = S::dot_rows(s_k, kb * 16 + c, g, qf);
-      const f32x4 dp = S::dot_rows(s_v, kb * 16 + c, g, dof);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float pr = fast_exp2(fmaf(st[r], sl2, -lse2));
-        if (j == i && kb * 16 + 4 * g + r > q_in_blk) pr = 0.f;
-        ds[kb][r] = pr * (dp[r] - dd);
-      }
-    }
-    S::accumulate_pv(acc, s_kt, ds, c, g);
-  }
-
-  T *dqr = dq + head_off + q_row * HD;
-#pragma unroll
-  for (int db = 0; db < S::kDB; ++db) S::store4(dqr + db * 16 + 4 * g, acc[db] * scale);
+  P pol;
+  pol.wl = wl;
+  pol.q = q;
+  pol.k = k;
+  pol.v = v;
+  pol.dout = dout;
+  pol.lse = lse;
+  pol.dvec = dvec;
+  pol.dq = dq;
+  pol.seq = (int64_t)wl.n * BLK;
+  pol.sl2 = sl2;
+  pol.scale = scale;
+  pol.lds = lds;
+  pol.tid = threadIdx.x;
+  pol.c = threadIdx.x & 15;
+  pol.g = (threadIdx.x & 63) >> 4;
+  pol.q_in_blk = (threadIdx.x >> 6) * 16 + pol.c;
+  run_packet<G>(pol, first, count);
 }
 
 template <typename T, int BLK, int HD>
@@ -223,6 +324,7 @@ gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStre
   const T *v = static_cast<const T *>(f.v);
   const T *o = static_cast<const T *>(f.o);
   const T *dout = static_cast<const T *>(a.dout);
+  const int32_t *n_long = m.sched + sched_words(m.batch, m.n_blocks);   // [0] rows, [1] columns
 
   constexpr int kLanes = HD / (16 / sizeof(T));
   if (stages & kBwdPrep) {
@@ -232,19 +334,20 @@ gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStre
     gsa_status st = check_launch("bwd_pre_kernel");
     if (st != GSA_OK) return st;
   }
-  const unsigned grid = (unsigned)padded_grid(items);
   if (stages & kBwdDkdv) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, BLK, HD>), dim3(grid), dim3(S::kThreads), 0, stream, q, k, v, dout,
-                       f.lse, a.workspace, static_cast<T *>(a.dk), static_cast<T *>(a.dv), m.col_ptr, m.row_idx,
-                       m.work_col, f.heads, m.n_blocks, mask_cap(m.n_blocks), m.n_heads[0], m.n_heads[1], items,
-                       sl2, scale);
+    const WorkLists wl{m.work_col, m.col_ptr, m.row_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
+                       mask_cap(m.n_blocks)};
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream, q, k,
+                       v, dout, f.lse, a.workspace, static_cast<T *>(a.dk), static_cast<T *>(a.dv), wl, n_long + 1,
+                       items, sl2, scale);
     gsa_status st = check_launch("bwd_dkdv_kernel");
     if (st != GSA_OK) return st;
   }
   if (stages & kBwdDq) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, BLK, HD>), dim3(grid), dim3(S::kThreads), 0, stream, q, k, v, dout,
-                       f.lse, a.workspace, static_cast<T *>(a.dq), m.row_ptr, m.col_idx, m.work_row, f.heads,
-                       m.n_blocks, mask_cap(m.n_blocks), m.n_heads[0], m.n_heads[1], items, sl2, scale);
+    const WorkLists wl{m.work_row, m.row_ptr, m.col_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
+                       mask_cap(m.n_blocks)};
+    hipLaunchKernelGGL((bwd_dq_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream, q, k, v,
+                       dout, f.lse, a.workspace, static_cast<T *>(a.dq), wl, n_long, items, sl2, scale);
     gsa_status st = check_launch("bwd_dq_kernel");
     if (st != GSA_OK) return st;
   }

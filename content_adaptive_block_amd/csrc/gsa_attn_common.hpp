@@ -1,18 +1,26 @@
 // Tile primitives shared by the attention kernels (forward, dK/dV, dQ).
 //
-// A "tile" is one mask block: BLK token rows of HD features, contiguous in memory
-// ([B, H, T, d] layout, so a block of one head is a dense BLK x HD row-major matrix).
-// Each wave owns 16 rows of the workgroup's own block; the other operand's block is
-// staged in LDS, row-major ("rows") and/or transposed ("cols").
+// A "tile" is one mask block of one head: BLK token rows of HD features, contiguous in
+// memory ([B, H, T, d] layout), i.e. a dense BLK x HD row-major matrix.  Each wave owns
+// 16 rows of its workgroup's own block, kept in registers; the other side's tiles are
+// staged row-major in LDS and read two ways:
+//   dot_rows:      C[m][n] = sum_f LDS[m][f] * F[n][f]    (A = 16 staged rows, b128 reads;
+//                  B = the wave's register fragment F)    -> a C tile whose rows m are
+//                  staged tokens (4 per lane) and whose column n is one of the wave's rows
+//   accumulate_pv: Acc[f][n] += sum_m LDS[m][f] * C[m][n] (A = the staged tile transposed,
+//                  read with ds_read_b64_tr_b16; B = a C tile from dot_rows fed back)
+// The second product takes a lane's four C rows of two adjacent 16-row tiles as its eight
+// K-slots; the transposed read delivers the other operand in the same token order.
 //
-// Products used (16x16 MFMA tiles, see gsa_device.hpp for the lane layouts):
-//   dot_rows:      C[m][n] = sum_d LDSrows[m][d] * F[n][d]   (A from LDS, B from the
-//                  wave's register fragment F of its 16 rows)  -> C rows m = staged
-//                  block's tokens (4 per lane), column n = one of the wave's rows
-//   accumulate_pv: Acc[f][n] += sum_m LDScols[f][m] * C[m][n] (A from the transposed
-//                  LDS block, B = a C tile from dot_rows fed back in place)
-// The second product reads a lane's C rows 4g+r of 16-row tiles 2kk and 2kk+1 as its
-// eight K-slots, and the transposed operand with the same token order.
+// LDS tiles are unpadded; each 16-byte chunk of a row is stored at chunk ^ swz(row).
+// Tiles arrive by asynchronous global -> LDS copies (no register staging).  The
+// swizzle keeps both read forms free of bank conflicts (measured on gfx950: 128-byte rows
+// use (row >> 1) & 7, 256-byte rows ((row & 7) << 1) | ((row >> 3) & 1)).
+//
+// Lane layout of ds_read_b64_tr_b16 (measured on gfx950): within each group of 16 lanes,
+// lane i receives element i % 4 of the 8 bytes addressed by lane 4e + i / 4, for
+// e = 0..3.  Pointing lane j at row key0 + j / 4, columns f0 + 4 (j % 4) .. + 3 therefore
+// gives lane i the four values T[key0 + e][f0 + i].
 #pragma once
 
 #include <type_traits>
@@ -22,9 +30,41 @@
 
 namespace gsa {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int head_class(int h, int n_loc, int n_lit) {
   return h < n_loc ? 0 : (h < n_loc + n_lit ? 1 : 2);
 }
+
+// One work item: list `list[beg, end)` of block `blk` of head `sh` = s * H + h.
+struct WorkItem {
+  int64_t sh;
+  int blk, beg, end;
+  const int32_t *list;
+};
+
+// Where work items live: the work list (item indices (s*H + h)*N + blk) and the
+// per-(sample, class) list pointers (CSR rows or CSC columns).
+struct WorkLists {
+  const int32_t *work, *ptr, *idx;
+  int heads, n, n_loc, n_lit;
+  int64_t cap;
+  __device__ __forceinline__ WorkItem decode(int64_t pos) const {
+    const uint32_t item = (uint32_t)work[pos];
+    WorkItem it;
+    it.blk = (int)(item % (uint32_t)n);
+    const uint32_t sh = item / (uint32_t)n;
+    it.sh = sh;
+    const int h = (int)(sh % (uint32_t)heads);
+    const int64_t s = sh / (uint32_t)heads;
+    const int cls = head_class(h, n_loc, n_lit);
+    const int32_t *p = ptr + (s * 3 + cls) * (int64_t)(n + 1);
+    it.list = idx + (s * 3 + cls) * cap;
+    it.beg = p[it.blk];
+    it.end = p[it.blk + 1];
+    return it;
+  }
+};
 
 template <typename T, int BLK, int HD>
 struct AttnShape {
@@ -36,16 +76,27 @@ struct AttnShape {
   static constexpr int kKB = BLK / 16;                 // 16-row tiles of a staged block
   static constexpr int kDB = HD / 16;                  // 16-wide feature tiles
   static constexpr int kKS = kBf16 ? HD / 32 : HD / 4; // MFMA K-steps over the features
-  static constexpr int kVec = 16 / sizeof(T);          // elements per 16-byte access
-  static constexpr int kRowStride = HD + (kBf16 ? 8 : 4);   // padded LDS row (elements)
-  static constexpr int kTStride = BLK + (kBf16 ? 8 : 4);    // padded LDS column block
-  static constexpr int kRowChunks = BLK * HD / kVec;
-  static_assert(kRowChunks % kThreads == 0, "row staging must divide evenly");
+  static constexpr int kVec = 16 / sizeof(T);          // elements per 16-byte chunk
+  static constexpr int kRowBytes = HD * sizeof(T);
+  static constexpr int kChunks = kRowBytes / 16;       // chunks per row
+  static_assert(kChunks == 8 || kChunks == 16, "rows of 128 or 256 bytes");
+  static constexpr int kTileBytes = BLK * kRowBytes;
+  static constexpr int kTileChunks = BLK * kChunks;
+  static_assert(kTileChunks % kThreads == 0, "staging must divide evenly");
+  static constexpr int kChunksPerThread = kTileChunks / kThreads;
 
   using Frag = typename std::conditional<kBf16, bf16x8, float>::type;
   struct QFrag {
     Frag f[kKS];
   };
+
+  __device__ static __forceinline__ int swz(int row) {
+    return kChunks == 8 ? ((row >> 1) & 7) : (((row & 7) << 1) | ((row >> 3) & 1));
+  }
+  // Byte offset of 16-byte chunk `ch` of row `row` inside a staged tile.
+  __device__ static __forceinline__ int chunk_off(int row, int ch) {
+    return row * kRowBytes + ((ch ^ swz(row)) << 4);
+  }
 
   // Register fragment of one token row (this lane's n = c), K-slots of lane group g.
   __device__ static __forceinline__ void load_row_frag(QFrag &qf, const T *row, int g) {
@@ -58,100 +109,89 @@ struct AttnShape {
     }
   }
 
-  // Copies a BLK x HD block to LDS row-major (row stride kRowStride).
-  __device__ static __forceinline__ void stage_rows(T *lds, const T *src, int tid) {
+  // Asynchronous copy of a BLK x HD tile into LDS in the swizzled layout: every copy
+  // instruction fills 64 consecutive 16-byte LDS slots, so each lane fetches the global
+  // chunk whose swizzled home is its slot.  kTileCopies instructions per thread.
+  static constexpr int kTileCopies = kChunksPerThread;
+  __device__ static __forceinline__ void copy_tile(unsigned char *lds, const T *src, int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
+    const unsigned char *g = reinterpret_cast<const unsigned char *>(src);
 #pragma unroll
-    for (int it = 0; it < kRowChunks / kThreads; ++it) {
-      const int u = tid + it * kThreads;
-      const int row = u / (HD / kVec), col = (u % (HD / kVec)) * kVec;
-      *reinterpret_cast<u32x4 *>(lds + row * kRowStride + col) =
-          *reinterpret_cast<const u32x4 *>(src + row * HD + col);
+    for (int it = 0; it < kTileCopies; ++it) {
+      const int first = it * kThreads + wave * 64;          // first slot of this instruction
+      const int slot = first + lane;
+      const int row = slot / kChunks, phys = slot % kChunks;
+      copy16_to_lds(g + ((row * kChunks + (phys ^ swz(row))) << 4), lds + (first << 4));
     }
   }
 
-  // Copies a BLK x HD block to LDS transposed: lds[f * kTStride + token].
-  __device__ static __forceinline__ void stage_cols(T *lds, const T *src, int tid) {
-    if constexpr (kBf16) {
-      // Unit = 2 tokens x 8 features: two 16-byte loads, eight 4-byte LDS stores.
-      constexpr int kUnits = BLK * HD / 16;
-      static_assert(kUnits % kThreads == 0, "column staging must divide evenly");
-#pragma unroll
-      for (int it = 0; it < kUnits / kThreads; ++it) {
-        const int u = tid + it * kThreads;
-        const int m = u % (HD / 8), kp = u / (HD / 8);
-        const u32x4 r0 = *reinterpret_cast<const u32x4 *>(src + (2 * kp) * HD + 8 * m);
-        const u32x4 r1 = *reinterpret_cast<const u32x4 *>(src + (2 * kp + 1) * HD + 8 * m);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t a = r0[e], b = r1[e];
-          // feature 8m + 2e: (low half of a, low half of b); 8m + 2e + 1: the high halves
-          const uint32_t lo = (a & 0xFFFFu) | (b << 16);
-          const uint32_t hi = (a >> 16) | (b & 0xFFFF0000u);
-          *reinterpret_cast<uint32_t *>(lds + (8 * m + 2 * e) * kTStride + 2 * kp) = lo;
-          *reinterpret_cast<uint32_t *>(lds + (8 * m + 2 * e + 1) * kTStride + 2 * kp) = hi;
-        }
-      }
-    } else {
-      constexpr int kUnits = BLK * HD / 4;
-      static_assert(kUnits % kThreads == 0, "column staging must divide evenly");
-#pragma unroll
-      for (int it = 0; it < kUnits / kThreads; ++it) {
-        const int u = tid + it * kThreads;
-        const int m = u % (HD / 4), tok = u / (HD / 4);
-        const f32x4 r = *reinterpret_cast<const f32x4 *>(src + tok * HD + 4 * m);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lds[(4 * m + e) * kTStride + tok] = r[e];
-      }
-    }
-  }
-
-  // C tile (16 staged rows starting at `row0 = 16 * tile`, lane's row row0 + c as A)
-  // times the wave's fragment.
-  __device__ static __forceinline__ f32x4 dot_rows(const T *lds, int row, int g, const QFrag &qf) {
+  // C tile: staged rows 16*tile .. +15 (this lane's row = 16*tile + c) x the fragment.
+  __device__ static __forceinline__ f32x4 dot_rows(const unsigned char *lds, int row, int g, const QFrag &qf) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kBf16) {
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lds + row * kRowStride + ks * 32 + 8 * g);
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lds + chunk_off(row, 4 * ks + g));
         acc = mfma_bf16(a, qf.f[ks], acc);
       }
     } else {
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) acc = mfma_f32(lds[row * kRowStride + 4 * ks + g], qf.f[ks], acc);
+      for (int ks = 0; ks < kKS; ++ks) {
+        const float a = *reinterpret_cast<const float *>(lds + chunk_off(row, ks) + 4 * g);
+        acc = mfma_f32(a, qf.f[ks], acc);
+      }
     }
     return acc;
   }
 
-  // acc[db] += LDScols[db*16 + c][tokens] x C, C = kKB tiles of 16 staged tokens.
-  __device__ static __forceinline__ void accumulate_pv(f32x4 *acc, const T *lds_t, const f32x4 *cm,
-                                                        int c, int g) {
+  // The second product runs in parts of kPartTiles 16-token tiles (32 tokens for bf16,
+  // one MFMA K-step; 16 for fp32), so callers without a row-wide softmax can produce and
+  // consume C one part at a time.
+  static constexpr int kPartTiles = kBf16 ? 2 : 1;
+  static constexpr int kParts = kKB / kPartTiles;
+
+  // acc[db] += (staged tile)^T[db*16 + c][tokens of part] x C, cm = the part's C tiles.
+  __device__ static __forceinline__ void accumulate_part(f32x4 *acc, const unsigned char *lds, const f32x4 *cm,
+                                                          int part, int c, int g) {
     if constexpr (kBf16) {
+      // Lane j = c of group g addresses rows 32*part + 16h + 4g + j/4, features db*16 + 4(j%4).
+      const int row0 = 32 * part + 4 * g + (c >> 2), row1 = row0 + 16;
+      const int fq = 4 * (c & 3);
+      bf16x8 b;
 #pragma unroll
-      for (int kk = 0; kk < kKB / 2; ++kk) {
-        bf16x8 b;
+      for (int r = 0; r < 4; ++r) {
+        b[r] = to_bf16(cm[0][r]);
+        b[4 + r] = to_bf16(cm[1][r]);
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          b[r] = to_bf16(cm[2 * kk][r]);
-          b[4 + r] = to_bf16(cm[2 * kk + 1][r]);
-        }
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const T *rowp = lds_t + (db * 16 + c) * kTStride + 32 * kk + 4 * g;
-          const bf16x4 a0 = *reinterpret_cast<const bf16x4 *>(rowp);
-          const bf16x4 a1 = *reinterpret_cast<const bf16x4 *>(rowp + 16);
-          const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          acc[db] = mfma_bf16(a, b, acc[db]);
-        }
+      for (int db = 0; db < kDB; ++db) {
+        const int f = db * 16 + fq;
+        const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(lds + chunk_off(row0, f >> 3) + 2 * (f & 7)));
+        const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(lds + chunk_off(row1, f >> 3) + 2 * (f & 7)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = mfma_bf16(a, b, acc[db]);
       }
     } else {
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
+      for (int r = 0; r < 4; ++r) {
+        const int row = part * 16 + 4 * g + r;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int db = 0; db < kDB; ++db)
-            acc[db] = mfma_f32(lds_t[(db * 16 + c) * kTStride + kb * 16 + 4 * g + r], cm[kb][r], acc[db]);
+        for (int db = 0; db < kDB; ++db) {
+          const int f = db * 16 + c;
+          const float a = *reinterpret_cast<const float *>(lds + chunk_off(row, f >> 2) + 4 * (f & 3));
+          acc[db] = mfma_f32(a, cm[0][r], acc[db]);
+        }
+      }
     }
+  }
+
+  // acc[db] += (staged tile)^T[db*16 + c][tokens] x C, C = kKB tiles of 16 staged tokens.
+  __device__ static __forceinline__ void accumulate_pv(f32x4 *acc, const unsigned char *lds, const f32x4 *cm,
+                                                        int c, int g) {
+#pragma unroll
+    for (int part = 0; part < kParts; ++part) accumulate_part(acc, lds, cm + part * kPartTiles, part, c, g);
   }
 
   // Stores four consecutive features.
@@ -164,5 +204,61 @@ struct AttnShape {
     }
   }
 };
+
+// ---------------------------------------------------------------------------------------
+// Packet pipeline shared by the attention kernels.  A workgroup runs the items of its
+// packet (see packet_of) back to back; every item walks one list (a CSR row or a CSC
+// column) and each list entry's tiles arrive in one of two LDS stages by asynchronous
+// copies issued one step ahead -- across item boundaries too, together with the next
+// item's register operands.  The policy P supplies:
+//   struct Item { int64_t sh; int blk, beg, end; const int32_t *list; }
+//   Item decode(pos)                     the item at a work-list position
+//   operands(item)                       load the item's register operands
+//   begin(item)                          adopt them, clear the accumulators
+//   copy(item, entry, stage)             issue the copies of one list entry into `stage`
+//   compute(item, e, stage)              one list entry (e indexes item.list)
+//   finish(item)                         write the item's outputs (kStores vector stores)
+// Step order: wait for this step's copies, synchronise, issue the next step's operand
+// loads and copies, compute, and -- after an item's last entry -- store.  The stores of
+// the previous item are the only vector memory operations younger than a step's copies,
+// so waiting until at most kStores operations are outstanding completes the copies
+// without waiting for those stores.  A compiler barrier keeps that issue order.
+// ---------------------------------------------------------------------------------------
+template <int G, class P>
+__device__ __forceinline__ void run_packet(P &pol, int64_t first, int count) {
+  typename P::Item its[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k)
+    if (k < count) its[k] = pol.decode(first + k);
+  pol.operands(its[0]);
+  pol.copy(its[0], its[0].list[its[0].beg], 0);
+  int stage = 0;
+  bool after_store = false;
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    if (k >= count) break;
+    const typename P::Item &cur = its[k];
+    for (int e = cur.beg; e < cur.end; ++e) {
+      if (after_store)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(P::kStores));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+      if (e == cur.beg) pol.begin(cur);
+      const bool last = e + 1 == cur.end;
+      if (!last) {
+        pol.copy(cur, cur.list[e + 1], stage ^ 1);
+      } else if (k + 1 < G && k + 1 < count) {
+        pol.operands(its[k + 1]);
+        pol.copy(its[k + 1], its[k + 1].list[its[k + 1].beg], stage ^ 1);
+      }
+      asm volatile("" ::: "memory");
+      pol.compute(cur, e, stage);
+      after_store = last;
+      if (last) pol.finish(cur);
+      stage ^= 1;
+    }
+  }
+}
 
 }  // namespace gsa

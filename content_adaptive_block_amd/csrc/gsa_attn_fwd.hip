@@ -7,20 +7,23 @@
 // diagonal block.  Keys outside the kept blocks carry exactly zero weight in the dense
 // masked form, so visiting only the kept blocks gives the same result.
 //
-// Design (one workgroup per (sample, head, query block); BLK/16 waves, 16 query rows
-// each):
+// Design (one workgroup of BLK/16 waves per (sample, head, query block); each wave owns
+// 16 of its query rows):
 //   * The query rows of a wave stay in registers as the B operand of S^T = K Q^T, so
 //     each lane owns one query column of every score tile and its online-softmax state
-//     (running max m and a lane-partial sum l) without cross-lane traffic except two
-//     shuffles for the row max.
-//   * K_j is staged row-major and V_j transposed in LDS, once per kv-block, shared by all
-//     waves.  O^T = V^T P^T accumulates in fp32 registers; P re-enters the MFMA straight
-//     from the S^T accumulator (rounded to bf16 in the bf16 instance).
-//   * Scores are scaled by scale * log2(e) so every exponential is one exp2.
+//     (running max m and a lane-partial sum l); the row max needs two permlane swaps.
+//   * K_j and V_j stream row-major (swizzled) into two LDS stages by asynchronous
+//     global -> LDS copies, one kept block ahead of the one being computed.  O^T =
+//     V^T P^T reads V^T with transposing LDS loads and takes P straight from the S^T
+//     accumulator (rounded to bf16 in the bf16 instance).
+//   * Short rows run in packets of neighbouring query blocks (see packet_of), the next
+//     block's loads crossing item boundaries.
+//   * Scores are scaled by scale * log2(e) so every exponential is one exp2.  The
+//     reference max is raised only when a row's max exceeds it by more than 2^8; O and l
+//     share that reference, so the result is unchanged and most rescales are skipped.
 //   * Only the diagonal block applies the token-causal mask.  Rows are never empty: the
 //     diagonal block is always kept and a query always sees itself.
-//   * Workgroups run in the mask kernel's longest-row-first order, with runs of adjacent
-//     items kept on one XCD (see work_position).
+//   * Workgroups run in the mask kernel's longest-row-first order.
 #include <type_traits>
 
 #include "gsa_attn_common.hpp"
@@ -28,97 +31,127 @@
 namespace gsa {
 namespace {
 
+constexpr float kRescaleSlack = 8.0f;   // log2 units
+
+// Packet size: neighbouring query blocks share one workgroup when tiles are small.
 template <typename T, int BLK, int HD>
-__global__ __launch_bounds__(BLK / 16 * 64) void attn_fwd_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
-    float *__restrict__ lse, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const int32_t *__restrict__ work, int heads, int n, int64_t cap, int n_loc, int n_lit,
-    int64_t items, float sl2) {
+constexpr int fwd_group() {
+  return AttnShape<T, BLK, HD>::kTileBytes <= 8 * 1024 ? kGroup : 1;
+}
+
+template <typename T, int BLK, int HD>
+struct FwdPolicy {
   using S = AttnShape<T, BLK, HD>;
-  __shared__ __align__(16) T s_k[BLK * S::kRowStride];   // K_j, row-major
-  __shared__ __align__(16) T s_vt[HD * S::kTStride];     // V_j transposed: [d][key]
+  using Item = WorkItem;
+  static constexpr int kStageBytes = 2 * S::kTileBytes;
+  static constexpr int kStores = S::kDB;   // O stores (the LSE store comes on top)
 
-  const int64_t pos = work_position(blockIdx.x, items);
-  if (pos < 0) return;
-  const int64_t item = work[pos];
-  const int i = (int)(item % n);
-  const int64_t sh = item / n;
-  const int h = (int)(sh % heads);
-  const int64_t s = sh / heads;
-  const int cls = head_class(h, n_loc, n_lit);
-  const int32_t *rp = row_ptr + (s * 3 + cls) * (int64_t)(n + 1);
-  const int32_t *cidx = col_idx + (s * 3 + cls) * cap;
-  const int beg = rp[i], end = rp[i + 1];
+  WorkLists wl;
+  const T *q, *k, *v;
+  T *o;
+  float *lse;
+  int64_t seq;
+  float sl2;
+  unsigned char *lds;
+  int tid, c, g, q_in_blk;
 
-  const int64_t seq = (int64_t)n * BLK;
-  const int64_t head_off = sh * seq * HD;
-  const T *qh = q + head_off;
-  const T *kh = k + head_off;
-  const T *vh = v + head_off;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const int q_in_blk = wave * 16 + c;            // this lane's query row inside block i
-  const int64_t q_row = (int64_t)i * BLK + q_in_blk;
-
-  typename S::QFrag qf;
-  S::load_row_frag(qf, qh + q_row * HD, g);
-
+  typename S::QFrag qf, qn;
   f32x4 acc[S::kDB];
+  float m_run, l_part;
+
+  __device__ Item decode(int64_t pos) const { return wl.decode(pos); }
+  __device__ void operands(const Item &it) {
+    S::load_row_frag(qn, q + (it.sh * seq + (int64_t)it.blk * BLK + q_in_blk) * HD, g);
+  }
+  __device__ void begin(const Item &) {
+    qf = qn;
 #pragma unroll
-  for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
-
-  for (int e = beg; e < end; ++e) {
-    const int j = cidx[e];
-    __syncthreads();
-    S::stage_rows(s_k, kh + (int64_t)j * BLK * HD, tid);
-    S::stage_cols(s_vt, vh + (int64_t)j * BLK * HD, tid);
-    __syncthreads();
-
+    for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_part = 0.f;
+  }
+  __device__ void copy(const Item &it, int j, int stage) {
+    const int64_t off = (it.sh * seq + (int64_t)j * BLK) * HD;
+    unsigned char *dst = lds + stage * kStageBytes;
+    S::copy_tile(dst, k + off, tid);
+    S::copy_tile(dst + S::kTileBytes, v + off, tid);
+  }
+  __device__ void compute(const Item &it, int e, int stage) {
+    const unsigned char *lk = lds + stage * kStageBytes;
+    const unsigned char *lv = lk + S::kTileBytes;
     // S^T tile: lane holds keys kb*16 + 4g + r of query q_in_blk.
     f32x4 st[S::kKB];
 #pragma unroll
-    for (int kb = 0; kb < S::kKB; ++kb) st[kb] = S::dot_rows(s_k, kb * 16 + c, g, qf);
-
-    if (j == i) {
+    for (int kb = 0; kb < S::kKB; ++kb) st[kb] = S::dot_rows(lk, kb * 16 + c, g, qf);
+    if (e == it.end - 1) {   // the diagonal block is the last (largest) entry of row i
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (kb * 16 + 4 * g + r > q_in_blk) st[kb][r] = -INFINITY;
     }
-
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kb][r]);
-    mx = group_max4(mx);
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_part *= alpha;
+    mx = group_max4(mx) * sl2;
+    if (mx > m_run + kRescaleSlack) {
+      const float alpha = fast_exp2(m_run - mx);
+      m_run = mx;
+      l_part *= alpha;
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) acc[db] *= alpha;
-
+      for (int db = 0; db < S::kDB; ++db) acc[db] *= alpha;
+    }
 #pragma unroll
     for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(fmaf(st[kb][r], sl2, -m_new));
+        const float p = fast_exp2(fmaf(st[kb][r], sl2, -m_run));
         st[kb][r] = p;
         l_part += p;
       }
-    S::accumulate_pv(acc, s_vt, st, c, g);
+    S::accumulate_pv(acc, lv, st, c, g);
   }
-
-  const float l = group_sum4(l_part);
-  const float inv = 1.0f / l;
-  T *oh = o + head_off + q_row * HD;
+  __device__ void finish(const Item &it) {
+    const float l = group_sum4(l_part);
+    const float inv = 1.0f / l;
+    const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk;
+    T *orow = o + q_row * HD;
 #pragma unroll
-  for (int db = 0; db < S::kDB; ++db) S::store4(oh + db * 16 + 4 * g, acc[db] * inv);
-  if (lse != nullptr && g == 0) lse[sh * seq + q_row] = (m_run + __log2f(l)) * 0.69314718055994531f;
+    for (int db = 0; db < S::kDB; ++db) S::store4(orow + db * 16 + 4 * g, acc[db] * inv);
+    if (lse != nullptr && g == 0) lse[q_row] = (m_run + __log2f(l)) * 0.69314718055994531f;
+  }
+};
+
+template <typename T, int BLK, int HD>
+__global__ __launch_bounds__(BLK / 16 * 64) void attn_fwd_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
+    float *__restrict__ lse, WorkLists wl, const int32_t *__restrict__ n_long_ptr, int64_t items,
+    float sl2) {
+  using P = FwdPolicy<T, BLK, HD>;
+  constexpr int G = fwd_group<T, BLK, HD>();
+  __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
+  int64_t first;
+  int count;
+  packet_of(blockIdx.x, items, G > 1 ? *n_long_ptr : items, G, &first, &count);
+  if (count == 0) return;
+
+  P pol;
+  pol.wl = wl;
+  pol.q = q;
+  pol.k = k;
+  pol.v = v;
+  pol.o = o;
+  pol.lse = lse;
+  pol.seq = (int64_t)wl.n * BLK;
+  pol.sl2 = sl2;
+  pol.lds = lds;
+  pol.tid = threadIdx.x;
+  pol.c = threadIdx.x & 15;
+  pol.g = (threadIdx.x & 63) >> 4;
+  pol.q_in_blk = (threadIdx.x >> 6) * 16 + pol.c;
+  run_packet<G>(pol, first, count);
 }
 
 template <typename T, int BLK, int HD>
@@ -127,11 +160,12 @@ gsa_status launch_fwd_instance(const gsa_fwd_args &a, const gsa_mask &m, hipStre
   const int64_t items = a.batch * a.heads * (int64_t)m.n_blocks;
   const float scale = a.scale > 0.f ? a.scale : 1.0f / sqrtf((float)HD);
   const float sl2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, BLK, HD>), dim3((unsigned)padded_grid(items)),
-                     dim3(S::kThreads), 0, stream, static_cast<const T *>(a.q),
-                     static_cast<const T *>(a.k), static_cast<const T *>(a.v), static_cast<T *>(a.o),
-                     a.lse, m.row_ptr, m.col_idx, m.work_row, a.heads, m.n_blocks, mask_cap(m.n_blocks),
-                     m.n_heads[0], m.n_heads[1], items, sl2);
+  const WorkLists wl{m.work_row, m.row_ptr, m.col_idx, a.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
+                     mask_cap(m.n_blocks)};
+  const int32_t *n_long = m.sched + sched_words(m.batch, m.n_blocks);   // row list
+  hipLaunchKernelGGL((attn_fwd_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream,
+                     static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
+                     static_cast<T *>(a.o), a.lse, wl, n_long, items, sl2);
   return check_launch("attn_fwd_kernel");
 }
 

@@ -39,13 +39,20 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
 // Reduce over the four lane groups that share a column (lanes c, c+16, c+32, c+48).
+// A permlane swap of a value with itself leaves, in its two results, each lane's own
+// value and that of the lane 16 (resp. 32) apart, so one ALU op per step reduces the
+// pair without a trip through the LDS crossbar.
 __device__ __forceinline__ float group_max4(float v) {
-  v = fmaxf(v, shfl_xor(v, 16));
-  return fmaxf(v, shfl_xor(v, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group_sum4(float v) {
-  v += shfl_xor(v, 16);
-  return v + shfl_xor(v, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -55,26 +62,65 @@ __device__ __forceinline__ bf16_t to_bf16(float x) { return (bf16_t)x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
 
 // ---------------------------------------------------------------------------------------
-// Workgroup order.  The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn,
-// and each XCD has its own L2.  Workgroups that reuse the same K/V tiles sit next to each
-// other in the work list, so runs of kChunk consecutive work-list positions are kept on
-// one XCD while successive runs still rotate over all XCDs (which keeps the longest-first
-// order balanced).  The grid is padded to a multiple of 8 * kChunk; ids mapping past the
-// end return -1.
+// Work packets.  The work list is ordered longest list first.  Items with at least
+// kSoloLen entries run one per workgroup; the rest run in packets of up to kGroup
+// consecutive positions -- in the list's order these are neighbouring blocks of one head
+// with lists of equal length, which share K/V tiles in the caches and share one stream
+// of loads, so the fixed cost of starting an item is paid once per packet.  The mask
+// kernel records the number of long items; the grid is sized for the worst case and
+// surplus workgroups return at once.
 // ---------------------------------------------------------------------------------------
-constexpr int kXcds = 8;
-constexpr int kChunk = 4;
+constexpr int kSoloLen = 8;
+constexpr int kGroup = 4;
 
-__host__ __device__ inline int64_t padded_grid(int64_t items) {
-  const int64_t q = (int64_t)kXcds * kChunk;
-  return (items + q - 1) / q * q;
+// First position and item count of workgroup b's packet (count 0: nothing to do).
+__device__ __forceinline__ void packet_of(int64_t b, int64_t items, int64_t n_long, int group,
+                                          int64_t *first, int *count) {
+  if (b < n_long) {
+    *first = b;
+    *count = 1;
+    return;
+  }
+  const int64_t f = n_long + (b - n_long) * group;
+  *first = f;
+  *count = f >= items ? 0 : (int)(items - f < group ? items - f : group);
 }
 
-__device__ __forceinline__ int64_t work_position(int64_t pid, int64_t items) {
-  const int64_t xcd = pid % kXcds;
-  const int64_t local = pid / kXcds;
-  const int64_t pos = ((local / kChunk) * kXcds + xcd) * kChunk + (local % kChunk);
-  return pos < items ? pos : -1;
+// ---------------------------------------------------------------------------------------
+// Asynchronous global -> LDS copies.  global_load_lds_dword{,x4} writes each active lane's
+// 4 or 16 bytes to LDS at (wave-uniform base) + lane * size; completion is tracked by
+// the wave's vmcnt like any vector load.  The compiler does not track which LDS bytes a
+// copy writes, so every read of copied data is preceded by an explicit vmcnt wait (and a
+// barrier, for the other waves' copies).
+// ---------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+__device__ __forceinline__ void copy16_to_lds(const void *g, unsigned char *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void copy4_to_lds(const void *g, unsigned char *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+}
+
+// s_waitcnt immediate for "vmcnt <= n" leaving the other counters alone (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Waits until at most `stride * k` of this wave's vector memory operations are still
+// outstanding, for a run-time k in [0, KMAX].
+template <int STRIDE, int KMAX>
+__device__ __forceinline__ void wait_vm_multiple(int k) {
+  static_assert(STRIDE * KMAX <= 63, "vmcnt range");
+  if constexpr (KMAX >= 3) {
+    if (k >= 3) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * STRIDE)); return; }
+  }
+  if constexpr (KMAX >= 2) {
+    if (k == 2) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * STRIDE)); return; }
+  }
+  if constexpr (KMAX >= 1) {
+    if (k == 1) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(STRIDE)); return; }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 }  // namespace gsa

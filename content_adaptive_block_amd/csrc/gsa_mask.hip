@@ -18,9 +18,17 @@
 // Column j: local i = j .. min(N-1, j+w); literal: literal i >= j if l_j, else j alone;
 // hybrid: i = j .. min(N-1, j+w) followed by (literal i > j + w, if l_j).
 //
-// Kernel 2 (two workgroups: rows and columns): a stable counting sort of every
-// (sample, head, block) item by list length, longest first, ties in ascending item
-// index.  It gives the launch order of the attention kernels.
+// Work order: every (sample, head, block) item sorted by list length, longest first, ties
+// in ascending item index (s*H + h)*N + i, once over CSR row lengths and once over CSC
+// column lengths.  Heads of one class share their lists, so the position of an item is
+// a closed form of per-(sample, class) data:
+//   pos(s, h, i) = start[len] + base[s][k][len] + (h - first head of k) * hist[s][k][len]
+//                  + rank[s][k][i]
+// where hist[s][k][len] counts the blocks of that length in the (s, k) lists, rank is the
+// number of earlier blocks of the same length there, base sums n_heads * hist over every
+// earlier (s', k') and start sums all items of every longer length.  Kernel 1 writes hist
+// and rank per sample; kernel 2 (one workgroup per list) scans them over lengths and
+// samples and scatters every item independently.
 #include "gsa_device.hpp"
 #include "gsa_internal.hpp"
 
@@ -57,13 +65,15 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
     const int32_t *__restrict__ c, int n, int w, uint8_t *__restrict__ flags,
     int32_t *__restrict__ n_literal, int32_t *__restrict__ row_ptr, int32_t *__restrict__ col_idx,
     int32_t *__restrict__ col_ptr, int32_t *__restrict__ row_idx, int64_t *__restrict__ n_edges,
-    int64_t cap) {
+    int64_t cap, int32_t *__restrict__ sched, int64_t batch) {
   __shared__ int s_prefix[GSA_MAX_BLOCKS + 1];   // # literal blocks before position i
   __shared__ int s_list[GSA_MAX_BLOCKS];         // literal block ids, ascending
   __shared__ int s_rstart[3][GSA_MAX_BLOCKS + 1];
   __shared__ int s_cstart[3][GSA_MAX_BLOCKS + 1];
   __shared__ long long s_sum[kMaskWaves];
   __shared__ int s_scan[kMaskWaves];
+  __shared__ int s_len[6][GSA_MAX_BLOCKS];       // row lengths (k), then column lengths (3 + k)
+  __shared__ int s_hist[6][GSA_MAX_BLOCKS + 1];
 
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int64_t s = blockIdx.x;
@@ -141,7 +151,44 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
       s_cstart[k][n] = tot;
     }
   }
+  // Per-(list, class) length histograms and stable ranks among equal lengths.
+  for (int x = t; x < 6 * (GSA_MAX_BLOCKS + 1); x += kMaskThreads) (&s_hist[0][0])[x] = 0;
+  if (t < n) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      s_len[k][t] = rlen[k];
+      s_len[3 + k][t] = clen[k];
+    }
+  }
   __syncthreads();
+  if (t < n) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      atomicAdd(&s_hist[k][rlen[k]], 1);
+      atomicAdd(&s_hist[3 + k][clen[k]], 1);
+    }
+  }
+  int rank6[6] = {0, 0, 0, 0, 0, 0};
+  if (t < n) {
+    int mine[6];
+#pragma unroll
+    for (int q = 0; q < 6; ++q) mine[q] = s_len[q][t];
+    for (int j2 = 0; j2 < t; ++j2) {
+#pragma unroll
+      for (int q = 0; q < 6; ++q) rank6[q] += s_len[q][j2] == mine[q] ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  {
+    const int seg = 3 * n + 2;
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const int list = q / 3, k = q % 3;
+      int32_t *sg = sched + ((list * batch + s) * 3 + k) * (int64_t)seg;
+      for (int l = t; l <= n; l += kMaskThreads) sg[l] = s_hist[q][l];
+      if (t < n) sg[2 * n + 2 + t] = rank6[q];
+    }
+  }
 
   // Rows: wave-per-row, lanes on consecutive entries.
   for (int k = 0; k < 3; ++k) {
@@ -176,92 +223,85 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
   }
 }
 
-constexpr int kSortThreads = 512;
-constexpr int kSortWaves = kSortThreads / kWave;
+constexpr int kSortThreads = 1024;
 
-// blockIdx.x == 0 sorts by CSR row length into work_row, 1 by CSC column length into
-// work_col.  Item index = (s * H + h) * N + i; bin = N - length (longest first).
+// blockIdx.x == 0 orders by CSR row length into work_row, 1 by CSC column length into
+// work_col.  See the work-order note at the top of this file.
 __global__ __launch_bounds__(kSortThreads) void worklist_kernel(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_ptr, int64_t batch, int n,
-    int n_loc, int n_lit, int n_hyb, int32_t *__restrict__ work_row, int32_t *__restrict__ work_col) {
-  __shared__ int s_cnt[kSortWaves][GSA_MAX_BLOCKS];
-  __shared__ int s_scan[kMaskWaves];
+    int n_loc, int n_lit, int n_hyb, int32_t *__restrict__ sched, int32_t *__restrict__ work_row,
+    int32_t *__restrict__ work_col) {
+  __shared__ int s_scan[kSortThreads / kWave];
 
-  const int32_t *ptr = blockIdx.x == 0 ? row_ptr : col_ptr;
-  int32_t *out = blockIdx.x == 0 ? work_row : work_col;
+  const int list = blockIdx.x;
+  const int32_t *ptr = list == 0 ? row_ptr : col_ptr;
+  int32_t *out = list == 0 ? work_row : work_col;
+  const int nh[3] = {n_loc, n_lit, n_hyb};
   const int heads = n_loc + n_lit + n_hyb;
-  const int64_t items = batch * heads * (int64_t)n;
+  const int seg = 3 * n + 2;
+  int32_t *base_list = sched + list * batch * 3 * (int64_t)seg;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int64_t nseg = batch * 3;
 
-  auto bin_of = [&](int64_t idx) -> int {
+  // Totals per length, over every sample and class, weighted by heads per class.  The
+  // (sample, class) loop is unrolled in groups so its loads are in flight together.
+  int tot = 0;
+  const int len = n - t;                 // thread t owns length n - t (bin t: longest first)
+  if (t < n) {
+    for (int64_t q0 = 0; q0 < nseg; q0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = q0 + u < nseg ? base_list[(q0 + u) * seg + len] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) tot += v[u] * (q0 + u < nseg ? nh[(q0 + u) % 3] : 0);
+    }
+  }
+  // Exclusive scan over bins (longest first) gives each length's start position.
+  int incl = tot;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) s_scan[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w2 = 0; w2 < wave; ++w2) wbase += s_scan[w2];
+  int running = wbase + incl - tot;
+  // Items with at least kSoloLen entries come first; their count tells the attention
+  // kernels where grouping starts.
+  if (len == kSoloLen - 1 && t < n) sched[sched_words(batch, n) + list] = running;
+  if (t == 0 && kSoloLen - 1 > n) sched[sched_words(batch, n) + list] = 0;
+  // base[s][k][len]: start of the first head of class k of sample s among this length.
+  if (t < n) {
+    for (int64_t q0 = 0; q0 < nseg; q0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = q0 + u < nseg ? base_list[(q0 + u) * seg + len] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (q0 + u < nseg) {
+          base_list[(q0 + u) * seg + n + 1 + len] = running;
+          running += v[u] * nh[(q0 + u) % 3];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // Scatter: every item computes its own position.
+  const int64_t items = batch * heads * (int64_t)n;
+  for (int64_t idx = t; idx < items; idx += kSortThreads) {
     const int i = (int)(idx % n);
     const int64_t sh = idx / n;
     const int h = (int)(sh % heads);
     const int64_t s = sh / heads;
     const int k = h < n_loc ? 0 : (h < n_loc + n_lit ? 1 : 2);
+    const int h0 = k == 0 ? 0 : (k == 1 ? n_loc : n_loc + n_lit);
     const int32_t *p = ptr + (s * 3 + k) * (int64_t)(n + 1);
-    return n - (p[i + 1] - p[i]);
-  };
-
-  for (int x = t; x < kSortWaves * GSA_MAX_BLOCKS; x += kSortThreads) (&s_cnt[0][0])[x] = 0;
-  __syncthreads();
-
-  const int64_t lo = items * wave / kSortWaves, hi = items * (wave + 1) / kSortWaves;
-  for (int64_t idx = lo + lane; idx < hi; idx += kWave) atomicAdd(&s_cnt[wave][bin_of(idx)], 1);
-  __syncthreads();
-
-  // Per bin: start = sum of all shorter-bin totals, then per-wave bases in wave order.
-  // Bins are scanned in rounds of kSortThreads.
-  int carry = 0;
-  for (int b0 = 0; b0 < n; b0 += kSortThreads) {
-    const int b = b0 + t;
-    int tot_b = 0;
-    if (b < n)
-      for (int w2 = 0; w2 < kSortWaves; ++w2) tot_b += s_cnt[w2][b];
-    // exclusive scan of tot_b over the 512 threads
-    int incl = tot_b;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      int y = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += y;
-    }
-    if (lane == kWave - 1) s_scan[wave] = incl;
-    __syncthreads();
-    int base = carry, round_tot = 0;
-    for (int w2 = 0; w2 < kSortWaves; ++w2) {
-      if (w2 < wave) base += s_scan[w2];
-      round_tot += s_scan[w2];
-    }
-    int start = base + incl - tot_b;
-    if (b < n) {
-      for (int w2 = 0; w2 < kSortWaves; ++w2) {
-        const int cnt = s_cnt[w2][b];
-        s_cnt[w2][b] = start;
-        start += cnt;
-      }
-    }
-    carry += round_tot;
-    __syncthreads();
-  }
-
-  // Stable scatter: each wave walks its chunk in order; lanes with equal bins are ranked
-  // by lane within each 64-item step, one distinct bin per pass.
-  for (int64_t base_idx = lo; base_idx < hi; base_idx += kWave) {
-    const int64_t idx = base_idx + lane;
-    const bool valid = idx < hi;
-    const int bin = valid ? bin_of(idx) : -1;
-    uint64_t active = __ballot(valid);
-    while (active) {
-      const int leader = __ffsll((unsigned long long)active) - 1;
-      const int lb = __shfl(bin, leader, kWave);
-      const uint64_t same = __ballot(valid && bin == lb) & active;
-      const int base = s_cnt[wave][lb];
-      if (valid && bin == lb && ((same >> lane) & 1ull)) {
-        out[base + __popcll(same & ((1ull << lane) - 1ull))] = (int32_t)idx;
-      }
-      if (lane == leader) s_cnt[wave][lb] = base + __popcll(same);
-      active &= ~same;
-    }
+    const int l = p[i + 1] - p[i];
+    const int32_t *sg = base_list + (s * 3 + k) * (int64_t)seg;
+    out[sg[n + 1 + l] + (h - h0) * sg[l] + sg[2 * n + 2 + i]] = (int32_t)idx;
   }
 }
 
@@ -271,12 +311,13 @@ gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t st
   const int n = m.n_blocks;
   hipLaunchKernelGGL(mask_kernel, dim3((unsigned)m.batch), dim3(kMaskThreads), 0, stream, c, n,
                      m.window, m.flags, m.n_literal, m.row_ptr, m.col_idx, m.col_ptr, m.row_idx,
-                     m.n_edges, mask_cap(n));
+                     m.n_edges, mask_cap(n), m.sched, m.batch);
   gsa_status st = check_launch("mask_kernel");
   if (st != GSA_OK) return st;
   if (m.n_heads[0] + m.n_heads[1] + m.n_heads[2] == 0) return GSA_OK;
   hipLaunchKernelGGL(worklist_kernel, dim3(2), dim3(kSortThreads), 0, stream, m.row_ptr, m.col_ptr,
-                     m.batch, n, m.n_heads[0], m.n_heads[1], m.n_heads[2], m.work_row, m.work_col);
+                     m.batch, n, m.n_heads[0], m.n_heads[1], m.n_heads[2], m.sched, m.work_row,
+                     m.work_col);
   return check_launch("worklist_kernel");
 }
 

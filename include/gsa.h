@@ -105,6 +105,9 @@ gsa_status gsa_prepare(const uint8_t *bytes, int64_t batch, int64_t seq_len, int
  *   work_row  int32 [B * H * N]       every (s, h, i) as (s*H + h)*N + i, longest CSR row
  *                                     first, ties in ascending index (forward and dQ order)
  *   work_col  int32 [B * H * N]       the same over CSC column lengths (dK/dV order)
+ *   sched     int32 [2*3*B*(3N+2)+8]  scratch of the work-order construction, and the
+ *                                     number of long items of each work list (read by
+ *                                     the attention calls; otherwise unspecified)
  * Entries of col_idx/row_idx past a segment's total are left untouched.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
@@ -121,11 +124,12 @@ typedef struct {
   int64_t *n_edges;
   int32_t *work_row;
   int32_t *work_col;
+  int32_t *sched;
 } gsa_mask;
 
-#define GSA_MASK_NBUF 9
+#define GSA_MASK_NBUF 10
 
-/* Byte sizes of the nine mask buffers, in the struct's field order (flags .. work_col). */
+/* Byte sizes of the ten mask buffers, in the struct's field order (flags .. sched). */
 gsa_status gsa_mask_sizes(int64_t batch, int32_t n_blocks, const int32_t n_heads[3],
                           size_t sizes_out[GSA_MASK_NBUF]);
 
@@ -141,8 +145,8 @@ gsa_status gsa_build_mask(const int32_t *c_dev, const gsa_mask *m, hipStream_t s
  *     off-diagonal kept blocks are fully visible.
  *
  *   q, k, v, o  device [B, H, T, d] contiguous, dtype GSA_BF16 or GSA_F32, 16-byte aligned
- *   lse         device fp32 [B, H, T]: natural-log sum of exp of the kept scaled scores;
- *               may be NULL when no backward follows
+ *   lse         device fp32 [B, H, T], 16-byte aligned: natural-log sum of exp of the kept
+ *               scaled scores; may be NULL when no backward follows
  *   scale       softmax scale; 0 selects 1/sqrt(d)
  * Built instances (dtype, block, head_dim): (F32, 16, 32), (BF16, 64, 64), (BF16, 128, 128).
  * Errors: NULL/misaligned pointers, heads != sum of mask head counts -> GSA_ERR_ARG;

@@ -75,7 +75,7 @@ def test_mask_sizes():
     sizes = gsa.gsa_mask_sizes(2, 5, (2, 1, 1))
     cap = 15
     assert sizes == [10, 8, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 8,
-                     2 * 4 * 5 * 4, 2 * 4 * 5 * 4]
+                     2 * 4 * 5 * 4, 2 * 4 * 5 * 4, (2 * 3 * 2 * (3 * 5 + 2) + 8) * 4]
     with pytest.raises(gsa.GsaError):
         gsa.gsa_mask_sizes(-1, 5, (1, 1, 1))
 
@@ -113,6 +113,7 @@ def test_build_mask_validation(lib):
     assert lib.gsa_build_mask(FAKE, ctypes.byref(_mask(heads=(1, -1, 1))), None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(FAKE, ctypes.byref(_mask(null=("col_idx",))), None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(FAKE, ctypes.byref(_mask(null=("flags",))), None) == gsa.GSA_ERR_ARG
+    assert lib.gsa_build_mask(FAKE, ctypes.byref(_mask(null=("sched",))), None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(None, ctypes.byref(_mask()), None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(FAKE, None, None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(None, ctypes.byref(_mask(batch=0)), None) == gsa.GSA_OK
@@ -131,6 +132,7 @@ def test_attn_fwd_validation(lib):
     assert _call_fwd(lib, _fwd(dtype=7), m) == gsa.GSA_ERR_ARG
     assert _call_fwd(lib, _fwd(null=("v",)), m) == gsa.GSA_ERR_ARG
     assert _call_fwd(lib, _fwd(misalign=("q",)), m) == gsa.GSA_ERR_ARG
+    assert _call_fwd(lib, _fwd(misalign=("lse",)), m) == gsa.GSA_ERR_ARG
     assert _call_fwd(lib, _fwd(scale=-1.0), m) == gsa.GSA_ERR_ARG
     assert _call_fwd(lib, _fwd(block=0), m) == gsa.GSA_ERR_ARG
     assert _call_fwd(lib, _fwd(), _mask(null=("work_row",))) == gsa.GSA_ERR_ARG
