@@ -2,8 +2,8 @@
 """Benchmark of the gzip-guided block-sparse attention hot path on one MI355X.
 
 One step = one pass of the device path over one batch: upload the per-block gzip
-sizes, build the mask (flags, CSR/CSC lists, work order), forward, and the three
-backward stages.  The host gzip stage (gsa_prepare) is timed separately on the host.
+sizes, build the mask (flags, CSR/CSC lists, work order), forward, and the two
+backward stages (dQ, which also forms D, then dK/dV).  The host gzip stage (gsa_prepare) is timed separately on the host.
 
 The workload is 8 samples x 8192 bytes, block 64, window 2, 12 heads (6 local /
 3 literal / 3 hybrid), head_dim 64, bf16, forward + backward, on seeded synthetic
@@ -34,7 +34,7 @@ METRIC = "effective TFLOP/s on kept blocks + fwd/bwd ms per batch at 8K bytes, %
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-KERNELS = ("mask", "fwd", "bwd_prep", "bwd_dkdv", "bwd_dq")
+KERNELS = ("mask", "fwd", "bwd_dq", "bwd_dkdv")   # in step order
 KERNEL_SOURCES = {"fwd": "gsa_attn_fwd.hip", "bwd_prep": "gsa_attn_bwd.hip", "bwd_dkdv": "gsa_attn_bwd.hip",
                   "bwd_dq": "gsa_attn_bwd.hip", "mask": "gsa_mask.hip"}
 
@@ -77,8 +77,8 @@ def kernel_work(name, wl, tiles):
         return 2 * x + r, 2 * wl.batch * wl.heads * wl.seq_len * d
     if name == "bwd_dkdv":         # read Q K V dO LSE D, write dK dV; S, dP, dV, dK
         return 6 * x + 2 * r, 8 * tile * tiles
-    if name == "bwd_dq":           # read Q K V dO LSE D, write dQ; S, dP, dQ
-        return 5 * x + 2 * r, 6 * tile * tiles
+    if name == "bwd_dq":           # read Q K V O dO LSE, write dQ D; S, dP, dQ, D
+        return 6 * x + 2 * r, 6 * tile * tiles + 2 * wl.batch * wl.heads * wl.seq_len * d
     n = wl.n_blocks
     return wl.batch * n * 4 * 2 + 3 * wl.batch * (2 * (n + 1) + n * (n + 1)) * 4, 0   # mask
 
@@ -206,7 +206,7 @@ def main():
         gsa.gsa_attn_fwd(t["q"], t["k"], t["v"], mask, wl.block, out=o, lse=lse)
         mark(2)
         if wl.backward:
-            for i, stage in enumerate(("prep", "dkdv", "dq")):
+            for i, stage in enumerate(("dq", "dkdv")):
                 gsa.gsa_attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], mask, wl.block, workspace=ws,
                                  out=grads, stage=stage)
                 mark(3 + i)
@@ -214,7 +214,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    n_ev = 6 if wl.backward else 3
+    n_ev = 5 if wl.backward else 3
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -240,7 +240,7 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
     fwd_ms = kern_ms["fwd"]
-    bwd_ms = sum(kern_ms.get(nm, 0.0) for nm in ("bwd_prep", "bwd_dkdv", "bwd_dq"))
+    bwd_ms = sum(kern_ms.get(nm, 0.0) for nm in ("bwd_dq", "bwd_dkdv"))
 
     kernels = {}
     for nm, ms in kern_ms.items():

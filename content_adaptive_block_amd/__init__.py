@@ -276,8 +276,9 @@ BWD_STAGES = {"all": "gsa_attn_bwd", "prep": "gsa_attn_bwd_prep", "dkdv": "gsa_a
 
 def gsa_attn_bwd(q, k, v, o, lse, dout, mask: GsaMask, block: int, scale: float = 0.0,
                  workspace=None, out=None, stage: str = "all"):
-    """dQ, dK, dV of sum(O * dout).  ``stage`` runs one backward stage only
-    ("prep", "dkdv" or "dq", in that order, sharing ``workspace`` and ``out``)."""
+    """dQ, dK, dV of sum(O * dout).  ``stage`` runs one backward stage only: "dq" (also
+    writes D into ``workspace``), then "dkdv" (reads it); "prep" writes D alone, for
+    running "dkdv" without "dq".  Stages share ``workspace`` and ``out``."""
     _check_tensors(q, k, v, o, dout)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
     if workspace is None:

@@ -122,7 +122,7 @@ gsa_status gsa_mask_sizes(int64_t batch, int32_t n_blocks, const int32_t n_heads
   sizes_out[6] = B * 3 * 8;                  // n_edges
   sizes_out[7] = B * H * N * 4;              // work_row
   sizes_out[8] = B * H * N * 4;              // work_col
-  sizes_out[9] = (size_t)(sched_words(batch, n_blocks) + 8) * 4;  // sched: scratch + long-item counts
+  sizes_out[9] = (size_t)sched_words(batch, n_blocks) * 4;  // sched: work-order scratch
   return GSA_OK;
 }
 

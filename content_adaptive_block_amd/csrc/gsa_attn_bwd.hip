@@ -8,16 +8,17 @@
 // forward's log-sum-exp, so nothing of size T x T is stored.
 //
 // Three kernels, all deterministic (no atomics; every output element has one writer):
-//   bwd_pre   D for every row (fp32).
+//   bwd_pre   D for every row (fp32), for callers that run dK/dV without dQ.
 //   bwd_dkdv  one workgroup per (sample, head, kv-block j), walking the CSC column of j
-//             (query blocks i that keep j); each wave keeps 16 keys of K_j, V_j in
+//             (query blocks i that keep j); each wave keeps 16 or 32 keys of K_j, V_j in
 //             registers and accumulates dK^T, dV^T tiles in fp32 while Q_i, dO_i, LSE_i
 //             and D_i stream through two LDS stages by asynchronous global -> LDS copies
 //             one block ahead; Q_i^T and dO_i^T come from transposing LDS reads.
 //   bwd_dq    one workgroup per (sample, head, query block i), walking the CSR row of i;
 //             each wave keeps 16 query rows of Q_i and dO_i in registers and accumulates
 //             dQ^T while K_j and V_j stream the same way (K_j^T by transposing reads).
-// Short lists run in packets of neighbouring blocks (see packet_of).
+//             It also forms D of its rows from O and dO and writes it for dK/dV, so the
+//             full backward runs dQ, then dK/dV, with no separate pass for D.
 #include <type_traits>
 
 #include "gsa_attn_common.hpp"
@@ -57,62 +58,51 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ o, c
   if (row < rows && part == 0) dvec[row] = acc;
 }
 
-// Packet size: neighbouring blocks share one workgroup when tiles are small.
+// 16-key groups per wave in dK/dV: two where registers allow, so that each LDS operand
+// read feeds two products.
 template <typename T, int BLK, int HD>
-constexpr int bwd_group() {
-  return AttnShape<T, BLK, HD>::kTileBytes <= 8 * 1024 ? kGroup : 1;
+constexpr int dkdv_groups() {
+  return std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0 ? 2 : 1;
 }
 
-// dK, dV of one (sample, head, kv-block j): walk the query blocks i of column j.
-template <typename T, int BLK, int HD>
+// dK, dV of one (sample, head, kv-block j): walk the query blocks i of column j.  Each
+// wave owns R groups of 16 keys of block j.
+template <typename T, int BLK, int HD, int R>
 struct DkdvPolicy {
-  using S = AttnShape<T, BLK, HD>;
+  using S = AttnShape<T, BLK, HD, R>;
   using Item = WorkItem;
   // A stage holds Q_i, dO_i, then LSE_i and D_i (BLK floats each).
   static constexpr int kStageBytes = 2 * S::kTileBytes + 2 * BLK * 4;
-  static constexpr int kStores = 2 * S::kDB;
-  // Each wave copies 16 of the BLK floats of LSE_i and of D_i (4-byte copies, 16 lanes).
-  static_assert(BLK == 16 * S::kWaves, "vector slice per wave");
-  // At d = 128 a wave's 256 registers cannot also hold the next item's K/V rows; those
-  // instances run one item per workgroup and load them directly.
-  static constexpr bool kAhead = HD <= 64;
-  struct NoFrag {};
-  using NextFrag = typename std::conditional<kAhead, typename S::QFrag, NoFrag>::type;
+  static constexpr int kVecLanes = BLK / S::kWaves;   // floats of LSE_i (and D_i) per wave
+  static_assert(kVecLanes <= 64, "vector slice per wave");
 
-  WorkLists wl;
   const T *q, *k, *v, *dout;
   const float *lse, *dvec;
   T *dk, *dv;
   int64_t seq;
   float sl2, scale;
   unsigned char *lds;
-  int tid, c, g, key_in_blk;
+  int tid, c, g, key0;   // key0: this lane's key of group 0 inside block j
 
-  typename S::QFrag kf, vf;
-  NextFrag kn, vn;
-  f32x4 dk_acc[S::kDB], dv_acc[S::kDB];
+  typename S::QFrag kf[R], vf[R];
+  f32x4 dk_acc[R][S::kDB], dv_acc[R][S::kDB];
 
-  __device__ Item decode(int64_t pos) const { return wl.decode(pos); }
   __device__ void operands(const Item &it) {
-    const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key_in_blk;
-    if constexpr (kAhead) {
-      S::load_row_frag(kn, k + key_row * HD, g);
-      S::load_row_frag(vn, v + key_row * HD, g);
-    } else {
-      S::load_row_frag(kf, k + key_row * HD, g);
-      S::load_row_frag(vf, v + key_row * HD, g);
+#pragma unroll
+    for (int kg = 0; kg < R; ++kg) {
+      const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key0 + 16 * kg;
+      S::load_row_frag(kf[kg], k + key_row * HD, g);
+      S::load_row_frag(vf[kg], v + key_row * HD, g);
     }
   }
   __device__ void begin(const Item &) {
-    if constexpr (kAhead) {
-      kf = kn;
-      vf = vn;
-    }
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) {
-      dk_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dv_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int kg = 0; kg < R; ++kg)
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db) {
+        dk_acc[kg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dv_acc[kg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
   }
   __device__ void copy(const Item &it, int i, int stage) {
     const int64_t row0 = it.sh * seq + (int64_t)i * BLK;
@@ -120,10 +110,10 @@ struct DkdvPolicy {
     S::copy_tile(dst, q + row0 * HD, tid);
     S::copy_tile(dst + S::kTileBytes, dout + row0 * HD, tid);
     const int wave = tid >> 6, lane = tid & 63;
-    if (lane < 16) {
-      const int x = wave * 16 + lane;
-      copy4_to_lds(lse + row0 + x, dst + 2 * S::kTileBytes + wave * 64);
-      copy4_to_lds(dvec + row0 + x, dst + 2 * S::kTileBytes + BLK * 4 + wave * 64);
+    if (lane < kVecLanes) {
+      const int x = wave * kVecLanes + lane;
+      copy4_to_lds(lse + row0 + x, dst + 2 * S::kTileBytes + wave * kVecLanes * 4);
+      copy4_to_lds(dvec + row0 + x, dst + 2 * S::kTileBytes + BLK * 4 + wave * kVecLanes * 4);
     }
   }
   __device__ void compute(const Item &it, int e, int stage) {
@@ -133,57 +123,69 @@ struct DkdvPolicy {
     const float *ld = ll + BLK;
     const bool diag = e == it.beg;   // column j starts with its own block i = j
     // P[q][key] and dS[q][key], one part of 16*kPartTiles queries at a time;
-    // lane: key c, queries qb*16 + 4g + r.
+    // lane: key c of each group, queries qb*16 + 4g + r.
 #pragma unroll
     for (int part = 0; part < S::kParts; ++part) {
-      f32x4 p[S::kPartTiles], ds[S::kPartTiles];
+      f32x4 p[R][S::kPartTiles], ds[R][S::kPartTiles];
 #pragma unroll
       for (int t = 0; t < S::kPartTiles; ++t) {
         const int qb = part * S::kPartTiles + t;
-        const f32x4 st = S::dot_rows(lq, qb * 16 + c, g, kf);
-        const f32x4 dp = S::dot_rows(ldo, qb * 16 + c, g, vf);
+        f32x4 st[R], dp[R];
+        if constexpr (R == 2) {
+          S::dot_rows2(lq, qb * 16 + c, g, kf[0], kf[1], st[0], st[1]);
+          S::dot_rows2(ldo, qb * 16 + c, g, vf[0], vf[1], dp[0], dp[1]);
+        } else {
+          st[0] = S::dot_rows(lq, qb * 16 + c, g, kf[0]);
+          dp[0] = S::dot_rows(ldo, qb * 16 + c, g, vf[0]);
+        }
         const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ll + qb * 16 + 4 * g);
         const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ld + qb * 16 + 4 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float pr = fast_exp2(fmaf(st[r], sl2, -l4[r] * kLog2e));
-          if (diag && key_in_blk > qb * 16 + 4 * g + r) pr = 0.f;
-          p[t][r] = pr;
-          ds[t][r] = pr * (dp[r] - d4[r]);
-        }
+        for (int kg = 0; kg < R; ++kg)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float pr = fast_exp2(fmaf(st[kg][r], sl2, -l4[r] * kLog2e));
+            if (diag && key0 + 16 * kg > qb * 16 + 4 * g + r) pr = 0.f;
+            p[kg][t][r] = pr;
+            ds[kg][t][r] = pr * (dp[kg][r] - d4[r]);
+          }
       }
-      S::accumulate_part(dv_acc, ldo, p, part, c, g);
-      S::accumulate_part(dk_acc, lq, ds, part, c, g);
+      if constexpr (R == 2) {
+        S::accumulate_part2(dv_acc[0], dv_acc[1], ldo, p[0], p[1], part, c, g);
+        S::accumulate_part2(dk_acc[0], dk_acc[1], lq, ds[0], ds[1], part, c, g);
+      } else {
+        S::accumulate_part(dv_acc[0], ldo, p[0], part, c, g);
+        S::accumulate_part(dk_acc[0], lq, ds[0], part, c, g);
+      }
     }
   }
   __device__ void finish(const Item &it) {
     // Lane holds features db*16 + 4g + r of its key: four consecutive features.
-    const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key_in_blk;
-    T *dkr = dk + key_row * HD;
-    T *dvr = dv + key_row * HD;
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) {
-      S::store4(dkr + db * 16 + 4 * g, dk_acc[db] * scale);
-      S::store4(dvr + db * 16 + 4 * g, dv_acc[db]);
+    for (int kg = 0; kg < R; ++kg) {
+      const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key0 + 16 * kg;
+      T *dkr = dk + key_row * HD;
+      T *dvr = dv + key_row * HD;
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db) {
+        S::store4(dkr + db * 16 + 4 * g, dk_acc[kg][db] * scale);
+        S::store4(dvr + db * 16 + 4 * g, dv_acc[kg][db]);
+      }
     }
   }
 };
 
 template <typename T, int BLK, int HD>
-__global__ __launch_bounds__(BLK / 16 * 64) void bwd_dkdv_kernel(
+__global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64)) void bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ dvec, T *__restrict__ dk, T *__restrict__ dv,
-    WorkLists wl, const int32_t *__restrict__ n_long_ptr, int64_t items, float sl2, float scale) {
-  using P = DkdvPolicy<T, BLK, HD>;
-  constexpr int G = bwd_group<T, BLK, HD>();
+    WorkLists wl, float sl2, float scale) {
+  constexpr int R = dkdv_groups<T, BLK, HD>();
+  using P = DkdvPolicy<T, BLK, HD, R>;
   __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
-  int64_t first;
-  int count;
-  packet_of(blockIdx.x, items, G > 1 ? *n_long_ptr : items, G, &first, &count);
-  if (count == 0) return;
+  const WorkItem it = wl.decode(blockIdx.x);
 
   P pol;
-  pol.wl = wl;
   pol.q = q;
   pol.k = k;
   pol.v = v;
@@ -199,44 +201,53 @@ __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dkdv_kernel(
   pol.tid = threadIdx.x;
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
-  pol.key_in_blk = (threadIdx.x >> 6) * 16 + pol.c;
-  run_packet<G>(pol, first, count);
+  pol.key0 = (threadIdx.x >> 6) * 16 * R + pol.c;
+  run_item(pol, it);
 }
 
-// dQ of one (sample, head, query block i): walk the kv-blocks j of row i.
+// dQ of one (sample, head, query block i): walk the kv-blocks j of row i.  The item's
+// D = rowsum(dO * O) is formed from the rows it loads anyway and written out for dK/dV.
 template <typename T, int BLK, int HD>
 struct DqPolicy {
   using S = AttnShape<T, BLK, HD>;
   using Item = WorkItem;
   static constexpr int kStageBytes = 2 * S::kTileBytes;
-  static constexpr int kStores = S::kDB;
 
-  WorkLists wl;
-  const T *q, *k, *v, *dout;
-  const float *lse, *dvec;
+  const T *q, *k, *v, *o, *dout;
+  const float *lse;
+  float *dvec;
   T *dq;
   int64_t seq;
   float sl2, scale;
   unsigned char *lds;
   int tid, c, g, q_in_blk;
 
-  typename S::QFrag qf, dof, qn, don;
-  float lse2, dd, lsen, ddn;
+  typename S::QFrag qf, dof;
+  float lse2, dd;
   f32x4 acc[S::kDB];
 
-  __device__ Item decode(int64_t pos) const { return wl.decode(pos); }
   __device__ void operands(const Item &it) {
     const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk;
-    S::load_row_frag(qn, q + q_row * HD, g);
-    S::load_row_frag(don, dout + q_row * HD, g);
-    lsen = lse[q_row];
-    ddn = dvec[q_row];
+    typename S::QFrag of;
+    S::load_row_frag(qf, q + q_row * HD, g);
+    S::load_row_frag(dof, dout + q_row * HD, g);
+    S::load_row_frag(of, o + q_row * HD, g);
+    lse2 = lse[q_row] * kLog2e;
+    // D over this lane's feature slots, then across the four lane groups of the row.
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < S::kKS; ++ks) {
+      if constexpr (S::kBf16) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) part = fmaf(to_f32(dof.f[ks][x]), to_f32(of.f[ks][x]), part);
+      } else {
+        part = fmaf(dof.f[ks], of.f[ks], part);
+      }
+    }
+    dd = group_sum4(part);
+    if (g == 0) dvec[q_row] = dd;
   }
   __device__ void begin(const Item &) {
-    qf = qn;
-    dof = don;
-    lse2 = lsen * kLog2e;
-    dd = ddn;
 #pragma unroll
     for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -280,22 +291,18 @@ struct DqPolicy {
 
 template <typename T, int BLK, int HD>
 __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dq_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dout,
-    const float *__restrict__ lse, const float *__restrict__ dvec, T *__restrict__ dq, WorkLists wl,
-    const int32_t *__restrict__ n_long_ptr, int64_t items, float sl2, float scale) {
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ o,
+    const T *__restrict__ dout, const float *__restrict__ lse, float *__restrict__ dvec, T *__restrict__ dq,
+    WorkLists wl, float sl2, float scale) {
   using P = DqPolicy<T, BLK, HD>;
-  constexpr int G = bwd_group<T, BLK, HD>();
   __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
-  int64_t first;
-  int count;
-  packet_of(blockIdx.x, items, G > 1 ? *n_long_ptr : items, G, &first, &count);
-  if (count == 0) return;
+  const WorkItem it = wl.decode(blockIdx.x);
 
   P pol;
-  pol.wl = wl;
   pol.q = q;
   pol.k = k;
   pol.v = v;
+  pol.o = o;
   pol.dout = dout;
   pol.lse = lse;
   pol.dvec = dvec;
@@ -308,12 +315,13 @@ __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dq_kernel(
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
   pol.q_in_blk = (threadIdx.x >> 6) * 16 + pol.c;
-  run_packet<G>(pol, first, count);
+  run_item(pol, it);
 }
 
 template <typename T, int BLK, int HD>
 gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream, int stages) {
   using S = AttnShape<T, BLK, HD>;
+  using SK = AttnShape<T, BLK, HD, dkdv_groups<T, BLK, HD>()>;
   const gsa_fwd_args &f = a.f;
   const int64_t items = f.batch * f.heads * (int64_t)m.n_blocks;
   const int64_t rows = f.batch * f.heads * f.seq_len;
@@ -324,7 +332,6 @@ gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStre
   const T *v = static_cast<const T *>(f.v);
   const T *o = static_cast<const T *>(f.o);
   const T *dout = static_cast<const T *>(a.dout);
-  const int32_t *n_long = m.sched + sched_words(m.batch, m.n_blocks);   // [0] rows, [1] columns
 
   constexpr int kLanes = HD / (16 / sizeof(T));
   if (stages & kBwdPrep) {
@@ -334,21 +341,21 @@ gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStre
     gsa_status st = check_launch("bwd_pre_kernel");
     if (st != GSA_OK) return st;
   }
-  if (stages & kBwdDkdv) {
-    const WorkLists wl{m.work_col, m.col_ptr, m.row_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
-                       mask_cap(m.n_blocks)};
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream, q, k,
-                       v, dout, f.lse, a.workspace, static_cast<T *>(a.dk), static_cast<T *>(a.dv), wl, n_long + 1,
-                       items, sl2, scale);
-    gsa_status st = check_launch("bwd_dkdv_kernel");
-    if (st != GSA_OK) return st;
-  }
   if (stages & kBwdDq) {
     const WorkLists wl{m.work_row, m.row_ptr, m.col_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
                        mask_cap(m.n_blocks)};
     hipLaunchKernelGGL((bwd_dq_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream, q, k, v,
-                       dout, f.lse, a.workspace, static_cast<T *>(a.dq), wl, n_long, items, sl2, scale);
+                       o, dout, f.lse, a.workspace, static_cast<T *>(a.dq), wl, sl2, scale);
     gsa_status st = check_launch("bwd_dq_kernel");
+    if (st != GSA_OK) return st;
+  }
+  if (stages & kBwdDkdv) {
+    const WorkLists wl{m.work_col, m.col_ptr, m.row_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
+                       mask_cap(m.n_blocks)};
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(SK::kThreads), 0, stream, q, k,
+                       v, dout, f.lse, a.workspace, static_cast<T *>(a.dk), static_cast<T *>(a.dv), wl, sl2,
+                       scale);
+    gsa_status st = check_launch("bwd_dkdv_kernel");
     if (st != GSA_OK) return st;
   }
   return GSA_OK;

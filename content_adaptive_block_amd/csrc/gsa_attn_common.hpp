@@ -66,12 +66,14 @@ struct WorkLists {
   }
 };
 
-template <typename T, int BLK, int HD>
+// R = 16-row groups owned by each wave (1 or 2); the workgroup has BLK / (16 R) waves.
+template <typename T, int BLK, int HD, int R = 1>
 struct AttnShape {
   static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static_assert(kBf16 || std::is_same<T, float>::value, "bf16 or fp32 only");
   static_assert(BLK % (kBf16 ? 32 : 16) == 0 && HD % (kBf16 ? 32 : 16) == 0, "tile shape");
-  static constexpr int kWaves = BLK / 16;
+  static_assert(R >= 1 && BLK % (16 * R) == 0, "row groups per wave");
+  static constexpr int kWaves = BLK / (16 * R);
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kKB = BLK / 16;                 // 16-row tiles of a staged block
   static constexpr int kDB = HD / 16;                  // 16-wide feature tiles
@@ -144,6 +146,21 @@ struct AttnShape {
     return acc;
   }
 
+  // Two C tiles of the same 16 staged rows against two fragments: one LDS read per K-step
+  // feeds both products.
+  __device__ static __forceinline__ void dot_rows2(const unsigned char *lds, int row, int g, const QFrag &f0,
+                                                   const QFrag &f1, f32x4 &c0, f32x4 &c1) {
+    c0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    c1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    static_assert(kBf16, "bf16 only");
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lds + chunk_off(row, 4 * ks + g));
+      c0 = mfma_bf16(a, f0.f[ks], c0);
+      c1 = mfma_bf16(a, f1.f[ks], c1);
+    }
+  }
+
   // The second product runs in parts of kPartTiles 16-token tiles (32 tokens for bf16,
   // one MFMA K-step; 16 for fp32), so callers without a row-wide softmax can produce and
   // consume C one part at a time.
@@ -187,6 +204,34 @@ struct AttnShape {
     }
   }
 
+  // accumulate_part for two C operands sharing the transposed LDS reads.
+  __device__ static __forceinline__ void accumulate_part2(f32x4 *acc0, f32x4 *acc1, const unsigned char *lds,
+                                                           const f32x4 *cm0, const f32x4 *cm1, int part, int c,
+                                                           int g) {
+    static_assert(kBf16, "bf16 only");
+    const int row0 = 32 * part + 4 * g + (c >> 2), row1 = row0 + 16;
+    const int fq = 4 * (c & 3);
+    bf16x8 b0, b1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      b0[r] = to_bf16(cm0[0][r]);
+      b0[4 + r] = to_bf16(cm0[1][r]);
+      b1[r] = to_bf16(cm1[0][r]);
+      b1[4 + r] = to_bf16(cm1[1][r]);
+    }
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      const int f = db * 16 + fq;
+      const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(lds + chunk_off(row0, f >> 3) + 2 * (f & 7)));
+      const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(lds + chunk_off(row1, f >> 3) + 2 * (f & 7)));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc0[db] = mfma_bf16(a, b0, acc0[db]);
+      acc1[db] = mfma_bf16(a, b1, acc1[db]);
+    }
+  }
+
   // acc[db] += (staged tile)^T[db*16 + c][tokens] x C, C = kKB tiles of 16 staged tokens.
   __device__ static __forceinline__ void accumulate_pv(f32x4 *acc, const unsigned char *lds, const f32x4 *cm,
                                                         int c, int g) {
@@ -206,59 +251,33 @@ struct AttnShape {
 };
 
 // ---------------------------------------------------------------------------------------
-// Packet pipeline shared by the attention kernels.  A workgroup runs the items of its
-// packet (see packet_of) back to back; every item walks one list (a CSR row or a CSC
-// column) and each list entry's tiles arrive in one of two LDS stages by asynchronous
-// copies issued one step ahead -- across item boundaries too, together with the next
-// item's register operands.  The policy P supplies:
-//   struct Item { int64_t sh; int blk, beg, end; const int32_t *list; }
-//   Item decode(pos)                     the item at a work-list position
-//   operands(item)                       load the item's register operands
-//   begin(item)                          adopt them, clear the accumulators
-//   copy(item, entry, stage)             issue the copies of one list entry into `stage`
-//   compute(item, e, stage)              one list entry (e indexes item.list)
-//   finish(item)                         write the item's outputs (kStores vector stores)
-// Step order: wait for this step's copies, synchronise, issue the next step's operand
-// loads and copies, compute, and -- after an item's last entry -- store.  The stores of
-// the previous item are the only vector memory operations younger than a step's copies,
-// so waiting until at most kStores operations are outstanding completes the copies
-// without waiting for those stores.  A compiler barrier keeps that issue order.
+// Per-item pipeline shared by the attention kernels.  A workgroup runs one work item,
+// which walks one list (a CSR row or a CSC column); each list entry's tiles arrive in
+// one of two LDS stages by asynchronous copies issued one entry ahead.  The policy P
+// supplies:
+//   operands(item)                 load the item's register operands (before the loop)
+//   begin(item)                    clear the accumulators
+//   copy(item, entry, stage)       issue the copies of one list entry into `stage`
+//   compute(item, e, stage)        one list entry (e indexes item.list)
+//   finish(item)                   write the item's outputs
+// A step waits for its own copies, synchronises -- after which every wave has finished
+// the previous step, so the other stage is free -- issues the next entry's copies and
+// computes.
 // ---------------------------------------------------------------------------------------
-template <int G, class P>
-__device__ __forceinline__ void run_packet(P &pol, int64_t first, int count) {
-  typename P::Item its[G];
-#pragma unroll
-  for (int k = 0; k < G; ++k)
-    if (k < count) its[k] = pol.decode(first + k);
-  pol.operands(its[0]);
-  pol.copy(its[0], its[0].list[its[0].beg], 0);
+template <class P>
+__device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
+  pol.operands(it);
+  pol.copy(it, it.list[it.beg], 0);
+  pol.begin(it);
   int stage = 0;
-  bool after_store = false;
-#pragma unroll
-  for (int k = 0; k < G; ++k) {
-    if (k >= count) break;
-    const typename P::Item &cur = its[k];
-    for (int e = cur.beg; e < cur.end; ++e) {
-      if (after_store)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(P::kStores));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      __syncthreads();
-      if (e == cur.beg) pol.begin(cur);
-      const bool last = e + 1 == cur.end;
-      if (!last) {
-        pol.copy(cur, cur.list[e + 1], stage ^ 1);
-      } else if (k + 1 < G && k + 1 < count) {
-        pol.operands(its[k + 1]);
-        pol.copy(its[k + 1], its[k + 1].list[its[k + 1].beg], stage ^ 1);
-      }
-      asm volatile("" ::: "memory");
-      pol.compute(cur, e, stage);
-      after_store = last;
-      if (last) pol.finish(cur);
-      stage ^= 1;
-    }
+  for (int e = it.beg; e < it.end; ++e) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    if (e + 1 < it.end) pol.copy(it, it.list[e + 1], stage ^ 1);
+    pol.compute(it, e, stage);
+    stage ^= 1;
   }
+  pol.finish(it);
 }
 
 }  // namespace gsa

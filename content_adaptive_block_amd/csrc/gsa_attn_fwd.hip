@@ -16,8 +16,6 @@
 //     global -> LDS copies, one kept block ahead of the one being computed.  O^T =
 //     V^T P^T reads V^T with transposing LDS loads and takes P straight from the S^T
 //     accumulator (rounded to bf16 in the bf16 instance).
-//   * Short rows run in packets of neighbouring query blocks (see packet_of), the next
-//     block's loads crossing item boundaries.
 //   * Scores are scaled by scale * log2(e) so every exponential is one exp2.  The
 //     reference max is raised only when a row's max exceeds it by more than 2^8; O and l
 //     share that reference, so the result is unchanged and most rescales are skipped.
@@ -33,18 +31,11 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 
-// Packet size: neighbouring query blocks share one workgroup when tiles are small.
-template <typename T, int BLK, int HD>
-constexpr int fwd_group() {
-  return AttnShape<T, BLK, HD>::kTileBytes <= 8 * 1024 ? kGroup : 1;
-}
-
 template <typename T, int BLK, int HD>
 struct FwdPolicy {
   using S = AttnShape<T, BLK, HD>;
   using Item = WorkItem;
   static constexpr int kStageBytes = 2 * S::kTileBytes;
-  static constexpr int kStores = S::kDB;   // O stores (the LSE store comes on top)
 
   WorkLists wl;
   const T *q, *k, *v;
@@ -55,16 +46,14 @@ struct FwdPolicy {
   unsigned char *lds;
   int tid, c, g, q_in_blk;
 
-  typename S::QFrag qf, qn;
+  typename S::QFrag qf;
   f32x4 acc[S::kDB];
   float m_run, l_part;
 
-  __device__ Item decode(int64_t pos) const { return wl.decode(pos); }
   __device__ void operands(const Item &it) {
-    S::load_row_frag(qn, q + (it.sh * seq + (int64_t)it.blk * BLK + q_in_blk) * HD, g);
+    S::load_row_frag(qf, q + (it.sh * seq + (int64_t)it.blk * BLK + q_in_blk) * HD, g);
   }
   __device__ void begin(const Item &) {
-    qf = qn;
 #pragma unroll
     for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run = -INFINITY;
@@ -127,15 +116,10 @@ struct FwdPolicy {
 template <typename T, int BLK, int HD>
 __global__ __launch_bounds__(BLK / 16 * 64) void attn_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
-    float *__restrict__ lse, WorkLists wl, const int32_t *__restrict__ n_long_ptr, int64_t items,
-    float sl2) {
+    float *__restrict__ lse, WorkLists wl, float sl2) {
   using P = FwdPolicy<T, BLK, HD>;
-  constexpr int G = fwd_group<T, BLK, HD>();
   __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
-  int64_t first;
-  int count;
-  packet_of(blockIdx.x, items, G > 1 ? *n_long_ptr : items, G, &first, &count);
-  if (count == 0) return;
+  const WorkItem it = wl.decode(blockIdx.x);
 
   P pol;
   pol.wl = wl;
@@ -151,7 +135,7 @@ __global__ __launch_bounds__(BLK / 16 * 64) void attn_fwd_kernel(
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
   pol.q_in_blk = (threadIdx.x >> 6) * 16 + pol.c;
-  run_packet<G>(pol, first, count);
+  run_item(pol, it);
 }
 
 template <typename T, int BLK, int HD>
@@ -162,10 +146,9 @@ gsa_status launch_fwd_instance(const gsa_fwd_args &a, const gsa_mask &m, hipStre
   const float sl2 = scale * 1.4426950408889634f;
   const WorkLists wl{m.work_row, m.row_ptr, m.col_idx, a.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
                      mask_cap(m.n_blocks)};
-  const int32_t *n_long = m.sched + sched_words(m.batch, m.n_blocks);   // row list
   hipLaunchKernelGGL((attn_fwd_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     static_cast<T *>(a.o), a.lse, wl, n_long, items, sl2);
+                     static_cast<T *>(a.o), a.lse, wl, sl2);
   return check_launch("attn_fwd_kernel");
 }
 

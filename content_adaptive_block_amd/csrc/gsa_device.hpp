@@ -1,5 +1,5 @@
 // Device-side building blocks for gfx950 (CDNA4): vector types, MFMA wrappers with their
-// lane layouts, wave reductions and the XCD-aware workgroup order.
+// lane layouts, wave reductions and asynchronous global -> LDS copies.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,31 +62,6 @@ __device__ __forceinline__ bf16_t to_bf16(float x) { return (bf16_t)x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
 
 // ---------------------------------------------------------------------------------------
-// Work packets.  The work list is ordered longest list first.  Items with at least
-// kSoloLen entries run one per workgroup; the rest run in packets of up to kGroup
-// consecutive positions -- in the list's order these are neighbouring blocks of one head
-// with lists of equal length, which share K/V tiles in the caches and share one stream
-// of loads, so the fixed cost of starting an item is paid once per packet.  The mask
-// kernel records the number of long items; the grid is sized for the worst case and
-// surplus workgroups return at once.
-// ---------------------------------------------------------------------------------------
-constexpr int kSoloLen = 8;
-constexpr int kGroup = 4;
-
-// First position and item count of workgroup b's packet (count 0: nothing to do).
-__device__ __forceinline__ void packet_of(int64_t b, int64_t items, int64_t n_long, int group,
-                                          int64_t *first, int *count) {
-  if (b < n_long) {
-    *first = b;
-    *count = 1;
-    return;
-  }
-  const int64_t f = n_long + (b - n_long) * group;
-  *first = f;
-  *count = f >= items ? 0 : (int)(items - f < group ? items - f : group);
-}
-
-// ---------------------------------------------------------------------------------------
 // Asynchronous global -> LDS copies.  global_load_lds_dword{,x4} writes each active lane's
 // 4 or 16 bytes to LDS at (wave-uniform base) + lane * size; completion is tracked by
 // the wave's vmcnt like any vector load.  The compiler does not track which LDS bytes a
@@ -105,22 +80,5 @@ __device__ __forceinline__ void copy4_to_lds(const void *g, unsigned char *lds_w
 // s_waitcnt immediate for "vmcnt <= n" leaving the other counters alone (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
-// Waits until at most `stride * k` of this wave's vector memory operations are still
-// outstanding, for a run-time k in [0, KMAX].
-template <int STRIDE, int KMAX>
-__device__ __forceinline__ void wait_vm_multiple(int k) {
-  static_assert(STRIDE * KMAX <= 63, "vmcnt range");
-  if constexpr (KMAX >= 3) {
-    if (k >= 3) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * STRIDE)); return; }
-  }
-  if constexpr (KMAX >= 2) {
-    if (k == 2) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * STRIDE)); return; }
-  }
-  if constexpr (KMAX >= 1) {
-    if (k == 1) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(STRIDE)); return; }
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-}
 
 }  // namespace gsa

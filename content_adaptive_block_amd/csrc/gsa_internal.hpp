@@ -20,8 +20,9 @@ gsa_status check_launch(const char *what);
 // Kernel launchers (arguments already validated).
 gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t stream);
 gsa_status launch_attn_fwd(const gsa_fwd_args &a, const gsa_mask &m, hipStream_t stream);
-// Backward stages: bit 0 = D precompute, bit 1 = dK/dV, bit 2 = dQ (run in that order).
-enum : int { kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7 };
+// Backward stages: bit 0 = D alone, bit 1 = dK/dV (reads D), bit 2 = dQ (writes D);
+// enqueued in the order D alone, dQ, dK/dV.
+enum : int { kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = kBwdDq | kBwdDkdv };
 gsa_status launch_attn_bwd(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream, int stages);
 
 // Whether a (dtype, block, head_dim) instance is compiled in.
@@ -29,8 +30,7 @@ bool attn_instance_built(int32_t dtype, int32_t block, int32_t head_dim);
 
 inline int64_t mask_cap(int32_t n) { return (int64_t)n * (n + 1) / 2; }
 
-// Int32 slots of the work-order scratch in the mask's sched buffer; two more slots after
-// them hold the number of long items of the row and column work lists.
+// Int32 slots of the work-order scratch in the mask's sched buffer.
 #if defined(__HIPCC__)
 #define GSA_HOST_DEVICE __host__ __device__
 #else

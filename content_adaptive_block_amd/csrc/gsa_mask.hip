@@ -268,10 +268,6 @@ __global__ __launch_bounds__(kSortThreads) void worklist_kernel(
   int wbase = 0;
   for (int w2 = 0; w2 < wave; ++w2) wbase += s_scan[w2];
   int running = wbase + incl - tot;
-  // Items with at least kSoloLen entries come first; their count tells the attention
-  // kernels where grouping starts.
-  if (len == kSoloLen - 1 && t < n) sched[sched_words(batch, n) + list] = running;
-  if (t == 0 && kSoloLen - 1 > n) sched[sched_words(batch, n) + list] = 0;
   // base[s][k][len]: start of the first head of class k of sample s among this length.
   if (t < n) {
     for (int64_t q0 = 0; q0 < nseg; q0 += 8) {

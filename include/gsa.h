@@ -105,9 +105,8 @@ gsa_status gsa_prepare(const uint8_t *bytes, int64_t batch, int64_t seq_len, int
  *   work_row  int32 [B * H * N]       every (s, h, i) as (s*H + h)*N + i, longest CSR row
  *                                     first, ties in ascending index (forward and dQ order)
  *   work_col  int32 [B * H * N]       the same over CSC column lengths (dK/dV order)
- *   sched     int32 [2*3*B*(3N+2)+8]  scratch of the work-order construction, and the
- *                                     number of long items of each work list (read by
- *                                     the attention calls; otherwise unspecified)
+ *   sched     int32 [2*3*B*(3N+2)]    scratch of the work-order construction (contents
+ *                                     unspecified after the call)
  * Entries of col_idx/row_idx past a segment's total are left untouched.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
@@ -194,12 +193,13 @@ typedef struct {
 
 gsa_status gsa_attn_bwd(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream);
 
-/* The three stages gsa_attn_bwd enqueues, in its order, for callers that time or
- * schedule them separately (same arguments, validation and errors as gsa_attn_bwd):
- *   gsa_attn_bwd_prep  D_t = sum_f dO_tf O_tf into a->workspace;
- *   gsa_attn_bwd_dkdv  dK, dV over the CSC column lists (reads D);
- *   gsa_attn_bwd_dq    dQ over the CSR row lists (reads D).
- * dkdv and dq are independent of each other once prep has run. */
+/* Stages of the backward, for callers that time or schedule them separately (same
+ * arguments, validation and errors as gsa_attn_bwd):
+ *   gsa_attn_bwd_dq    dQ over the CSR row lists; also writes D_t = sum_f dO_tf O_tf of
+ *                      every row into a->workspace;
+ *   gsa_attn_bwd_dkdv  dK, dV over the CSC column lists; reads D from a->workspace;
+ *   gsa_attn_bwd_prep  D alone, for running dK/dV without dQ.
+ * gsa_attn_bwd enqueues gsa_attn_bwd_dq, then gsa_attn_bwd_dkdv. */
 gsa_status gsa_attn_bwd_prep(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream);
 gsa_status gsa_attn_bwd_dkdv(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream);
 gsa_status gsa_attn_bwd_dq(const gsa_bwd_args *a, const gsa_mask *m, hipStream_t stream);

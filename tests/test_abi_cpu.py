@@ -75,7 +75,7 @@ def test_mask_sizes():
     sizes = gsa.gsa_mask_sizes(2, 5, (2, 1, 1))
     cap = 15
     assert sizes == [10, 8, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 8,
-                     2 * 4 * 5 * 4, 2 * 4 * 5 * 4, (2 * 3 * 2 * (3 * 5 + 2) + 8) * 4]
+                     2 * 4 * 5 * 4, 2 * 4 * 5 * 4, 2 * 3 * 2 * (3 * 5 + 2) * 4]
     with pytest.raises(gsa.GsaError):
         gsa.gsa_mask_sizes(-1, 5, (1, 1, 1))
 

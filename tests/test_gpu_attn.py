@@ -198,3 +198,42 @@ def test_full_size_sampled(cid):
         got = np.concatenate([p[0].ravel() for p in pairs])
         ref = np.concatenate([p[1].ravel() for p in pairs])
         assert_close(f"{nm} ({len(pairs)} sampled blocks)", got, ref, ltol if nm == "LSE" else tol)
+
+
+@pytest.mark.parametrize("inst", list(BASE))
+def test_backward_stage_entry_points(inst):
+    """dq then dkdv equals the whole backward bit for bit; dq writes D = rowsum(dO * O);
+    prep then dkdv gives dK, dV within tolerance (D summed in another order)."""
+    dtype, block, hd = inst
+    n_heads, window, batch, n = (2, 1, 1), 2, 2, 7
+    log(f"  stages {dtype} b={block} d={hd}")
+    x, t = _inputs(inst, batch, n, sum(n_heads))
+    res = run_path(x, block, window, n_heads, t, backward=True)
+    q, k, v, do = (t[nm].cuda() for nm in ("q", "k", "v", "do"))
+    o, lse, m = res["o"], res["lse"], res["mask"]
+
+    ws = torch.full_like(lse, float("nan"))
+    g = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    gsa.gsa_attn_bwd(q, k, v, o, lse, do, m, block, workspace=ws, out=g, stage="dq")
+    torch.cuda.synchronize()
+    assert torch.isnan(g[1]).all() and torch.isnan(g[2]).all()
+    d_ref = (f64(do) * f64(o)).sum(axis=-1)
+    assert_close("D from dq", f64(ws), d_ref, 1e-4 if dtype == "bf16" else F32_TOL)
+    gsa.gsa_attn_bwd(q, k, v, o, lse, do, m, block, workspace=ws, out=g, stage="dkdv")
+    torch.cuda.synchronize()
+    for nm, got in zip(("dq", "dk", "dv"), g):
+        assert torch.equal(got, res[nm]), nm
+
+    ws2 = torch.full_like(lse, float("nan"))
+    g2 = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    gsa.gsa_attn_bwd(q, k, v, o, lse, do, m, block, workspace=ws2, out=g2, stage="prep")
+    gsa.gsa_attn_bwd(q, k, v, o, lse, do, m, block, workspace=ws2, out=g2, stage="dkdv")
+    torch.cuda.synchronize()
+    assert torch.isnan(g2[0]).all()
+    assert_close("D from prep", f64(ws2), d_ref, 1e-4 if dtype == "bf16" else F32_TOL)
+    masks = _oracle_masks(x, block, window)
+    _, ref_dk, ref_dv = oracle.attn_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), masks, n_heads,
+                                        block)
+    tol, _ = _tol(dtype)
+    assert_close("dK after prep", f64(g2[1]), ref_dk, tol)
+    assert_close("dV after prep", f64(g2[2]), ref_dv, tol)
