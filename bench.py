@@ -96,6 +96,58 @@ def load_traffic(name: str, wl) -> float | None:
     return float(rec["bytes_per_launch"])
 
 
+PMC_KERNELS = {"attn_fwd_kernel": "fwd", "bwd_dq_kernel": "bwd_dq", "bwd_dkdv_kernel": "bwd_dkdv",
+               "bwd_pre_kernel": "bwd_prep"}
+
+
+def _pmc_means(path: str, counter: str) -> dict:
+    """Mean counter value (KiB) per dispatch for each kernel of a rocprofv3 counter_collection.csv."""
+    import csv
+    vals: dict = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = next((v for k, v in PMC_KERNELS.items() if k in name), None)
+            if key is None and "neg_kernel" in name:
+                key = "copy"
+            if key is not None:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: (float(np.mean(v)), len(v)) for k, v in vals.items()}
+
+
+def record_traffic(args, fetch_csv: str, write_csv: str):
+    """Per-launch HBM bytes of each attention kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the calibration copy of
+    --copy-mib MiB, written to profiles/traffic_<kernel>_<workload>.json."""
+    import synth
+    wl = synth.WORKLOADS[args.config]
+    if args.copy_mib <= 0:
+        raise SystemExit("--traffic-from needs the --copy-mib of the profiled run")
+    fetch, write = _pmc_means(fetch_csv, "FETCH_SIZE"), _pmc_means(write_csv, "WRITE_SIZE")
+    copy_bytes = float(args.copy_mib << 20)
+    scale_f = copy_bytes / (fetch["copy"][0] * 1024.0)
+    scale_w = copy_bytes / (write["copy"][0] * 1024.0)
+    rows = []
+    for name in sorted(set(fetch) & set(write) - {"copy"}):
+        fb, wb = fetch[name][0] * 1024.0 * scale_f, write[name][0] * 1024.0 * scale_w
+        rec = {"kernel": name, "workload": wl.name, "bytes_per_launch": round(fb + wb),
+               "fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": fetch[name][1],
+               "fetch_scale": round(scale_f, 4), "write_scale": round(scale_w, 4),
+               "copy_mib": args.copy_mib, "source_hash": kernel_source_hash(name)}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{name}_{wl.name}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        rows.append(rec)
+    print(f"| kernel | dispatches | FETCH bytes | WRITE bytes | HBM bytes / launch |")
+    print(f"|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['kernel']} | {r['dispatches']} | {r['fetch_bytes']:,} | {r['write_bytes']:,} | "
+              f"{r['bytes_per_launch']:,} |")
+    print(f"\nscale: FETCH x {scale_f:.4f}, WRITE x {scale_w:.4f} (copy of {args.copy_mib} MiB)")
+
+
 def cpu_baseline(wl, x_bytes, tensors, masks_np, budget_s: float):
     """The fp64 oracle on whole heads of sample 0 until ``budget_s`` seconds are spent."""
     import oracle
@@ -143,8 +195,14 @@ def main():
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5); 4 is the headline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
-                    help="only run a plain device copy of this many MiB 5 times (HBM counter calibration)")
+                    help="first run a plain elementwise copy of this many MiB 3 times (HBM counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then "
+                         "WRITE_SIZE, of a run with --copy-mib) into per-launch HBM bytes under profiles/")
     args = ap.parse_args()
+    if args.traffic_from:
+        record_traffic(args, *args.traffic_from)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -160,14 +218,13 @@ def main():
     wl = synth.WORKLOADS[args.config]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    if args.copy_mib > 0:
+    if args.copy_mib > 0:   # reads and writes copy_mib MiB per launch, 16-byte vector accesses
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4}))
-        return
+        del src, dst
 
     x = synth.gen_bytes(wl)
     names = ("q", "k", "v", "do") if wl.backward else ("q", "k", "v")

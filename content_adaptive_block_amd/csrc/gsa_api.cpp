@@ -32,7 +32,7 @@ gsa_status check_launch(const char *what) {
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-static gsa_status check_mask(const gsa_mask *m, bool need_flags) {
+static gsa_status check_mask(const gsa_mask *m, bool building) {
   if (!m) return fail(GSA_ERR_ARG, "mask is NULL");
   if (m->batch < 0) return fail(GSA_ERR_ARG, "mask batch %lld < 0", (long long)m->batch);
   if (m->window < 0) return fail(GSA_ERR_ARG, "window %d < 0", m->window);
@@ -43,9 +43,9 @@ static gsa_status check_mask(const gsa_mask *m, bool need_flags) {
     return fail(GSA_ERR_UNSUPPORTED, "n_blocks %d outside 1..%d", m->n_blocks, GSA_MAX_BLOCKS);
   if (!m->row_ptr || !m->col_idx || !m->col_ptr || !m->row_idx || !m->work_row || !m->work_col)
     return fail(GSA_ERR_ARG, "mask list buffer is NULL");
-  if (!m->sched) return fail(GSA_ERR_ARG, "mask sched buffer is NULL");
-  if (need_flags && (!m->flags || !m->n_literal || !m->n_edges))
-    return fail(GSA_ERR_ARG, "mask flag/count buffer is NULL");
+  if (building && (!m->flags || !m->n_literal || !m->n_edges || !m->sched))
+    return fail(GSA_ERR_ARG, "mask flag/count/sched buffer is NULL");
+  if (building && !aligned16(m->sched)) return fail(GSA_ERR_ARG, "mask sched buffer is not 16-byte aligned");
   int64_t items = m->batch * (int64_t)(m->n_heads[0] + m->n_heads[1] + m->n_heads[2]) * m->n_blocks;
   if (items > INT32_MAX) return fail(GSA_ERR_UNSUPPORTED, "B*H*N = %lld exceeds int32", (long long)items);
   return GSA_OK;

@@ -60,9 +60,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ o, c
 
 // 16-key groups per wave in dK/dV: two where registers allow, so that each LDS operand
 // read feeds two products.
+#ifndef GSA_DKDV_GROUPS
+#define GSA_DKDV_GROUPS 2
+#endif
 template <typename T, int BLK, int HD>
 constexpr int dkdv_groups() {
-  return std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0 ? 2 : 1;
+  return std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0 ? GSA_DKDV_GROUPS : 1;
 }
 
 // dK, dV of one (sample, head, kv-block j): walk the query blocks i of column j.  Each
@@ -183,7 +186,7 @@ __global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64)) void
   constexpr int R = dkdv_groups<T, BLK, HD>();
   using P = DkdvPolicy<T, BLK, HD, R>;
   __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
-  const WorkItem it = wl.decode(blockIdx.x);
+  const WorkItem it = wl.decode(dispatch_position(blockIdx.x, gridDim.x));
 
   P pol;
   pol.q = q;
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dq_kernel(
     WorkLists wl, float sl2, float scale) {
   using P = DqPolicy<T, BLK, HD>;
   __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
-  const WorkItem it = wl.decode(blockIdx.x);
+  const WorkItem it = wl.decode(dispatch_position(blockIdx.x, gridDim.x));
 
   P pol;
   pol.q = q;

@@ -66,6 +66,26 @@ struct WorkLists {
   }
 };
 
+// Work position of workgroup b of a grid of `total`.  Workgroups are handed to the eight
+// XCDs round-robin (b % 8) and each XCD has its own L2; with a chunk C > 0, every window
+// of 8C consecutive work positions is split into eight runs of C, one per XCD, so that
+// neighbouring items (which share kv-blocks) meet in one L2 while the window order keeps
+// the longest-first schedule.  The tail past the last whole window keeps its order.
+#ifndef GSA_XCD_CHUNK
+#define GSA_XCD_CHUNK 16
+#endif
+__device__ __forceinline__ uint32_t dispatch_position(uint32_t b, uint32_t total) {
+  constexpr uint32_t kX = 8, kC = GSA_XCD_CHUNK;
+  if constexpr (kC == 0) {
+    return b;
+  } else {
+    constexpr uint32_t kW = kX * kC;
+    if (b >= total / kW * kW) return b;
+    const uint32_t r = b % kW;
+    return b - r + (r % kX) * kC + r / kX;
+  }
+}
+
 // R = 16-row groups owned by each wave (1 or 2); the workgroup has BLK / (16 R) waves.
 template <typename T, int BLK, int HD, int R = 1>
 struct AttnShape {

@@ -21,7 +21,8 @@
 //     share that reference, so the result is unchanged and most rescales are skipped.
 //   * Only the diagonal block applies the token-causal mask.  Rows are never empty: the
 //     diagonal block is always kept and a query always sees itself.
-//   * Workgroups run in the mask kernel's longest-row-first order.
+//   * Workgroups run in the mask kernel's work order (longest rows first, by octave of
+//     length), runs of 16 consecutive items per XCD.
 #include <type_traits>
 
 #include "gsa_attn_common.hpp"
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(BLK / 16 * 64) void attn_fwd_kernel(
     float *__restrict__ lse, WorkLists wl, float sl2) {
   using P = FwdPolicy<T, BLK, HD>;
   __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
-  const WorkItem it = wl.decode(blockIdx.x);
+  const WorkItem it = wl.decode(dispatch_position(blockIdx.x, gridDim.x));
 
   P pol;
   pol.wl = wl;

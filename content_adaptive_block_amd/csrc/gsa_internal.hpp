@@ -30,12 +30,16 @@ bool attn_instance_built(int32_t dtype, int32_t block, int32_t head_dim);
 
 inline int64_t mask_cap(int32_t n) { return (int64_t)n * (n + 1) / 2; }
 
-// Int32 slots of the work-order scratch in the mask's sched buffer.
+// Work-order scratch in the mask's sched buffer (int32 words): per (list, sample, class)
+// a histogram and a base over kOrderKeys length keys, then one packed rank/key per block.
+constexpr int kOrderKeys = 16;
 #if defined(__HIPCC__)
 #define GSA_HOST_DEVICE __host__ __device__
 #else
 #define GSA_HOST_DEVICE
 #endif
-GSA_HOST_DEVICE inline int64_t sched_words(int64_t batch, int32_t n) { return 2 * 3 * batch * (3 * (int64_t)n + 2); }
+GSA_HOST_DEVICE inline int64_t sched_words(int64_t batch, int32_t n) {
+  return 2 * 3 * batch * ((int64_t)n + 2 * kOrderKeys);
+}
 
 }  // namespace gsa

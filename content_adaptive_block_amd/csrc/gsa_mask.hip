@@ -10,25 +10,26 @@
 //
 // Kernel 1 (one workgroup of 1024 threads per sample, one thread per block): the sum of
 // c, the flags, literal ranks by wave ballot + popcount prefix, row and column lengths
-// in closed form, exclusive scans into row_ptr/col_ptr, then every wave writes whole
-// rows (and columns) with its 64 lanes on consecutive entries.  Row i of each class:
+// in closed form, one combined exclusive scan into row_ptr/col_ptr, then every list
+// entry is written by its own thread (row found by binary search over the row starts).
+// Row i of each class:
 //   local   : j = max(0, i-w) .. i
 //   literal : literal j <= i if l_i, else i alone
 //   hybrid  : (literal j < i - w, if l_i) followed by j = max(0, i-w) .. i
 // Column j: local i = j .. min(N-1, j+w); literal: literal i >= j if l_j, else j alone;
 // hybrid: i = j .. min(N-1, j+w) followed by (literal i > j + w, if l_j).
 //
-// Work order: every (sample, head, block) item sorted by list length, longest first, ties
-// in ascending item index (s*H + h)*N + i, once over CSR row lengths and once over CSC
-// column lengths.  Heads of one class share their lists, so the position of an item is
-// a closed form of per-(sample, class) data:
-//   pos(s, h, i) = start[len] + base[s][k][len] + (h - first head of k) * hist[s][k][len]
-//                  + rank[s][k][i]
-// where hist[s][k][len] counts the blocks of that length in the (s, k) lists, rank is the
-// number of earlier blocks of the same length there, base sums n_heads * hist over every
-// earlier (s', k') and start sums all items of every longer length.  Kernel 1 writes hist
-// and rank per sample; kernel 2 (one workgroup per list) scans them over lengths and
-// samples and scatters every item independently.
+// Work order: every (sample, head, block) item sorted by the octave of its list length,
+// key = floor(log2 len) + 1, largest first, ties in ascending item index (s*H + h)*N + i,
+// once over CSR row lengths and once over CSC column lengths.  Heads of one class share
+// their lists, so the position of an item is a closed form of per-(sample, class) data:
+//   pos(s, h, i) = base[s][k][key] + (h - first head of k) * hist[s][k][key] + rank[s][k][i]
+// where hist[s][k][key] counts the blocks with that key in the (s, k) list, rank is the
+// number of earlier blocks with the same key there (found by ballots over the key bits),
+// and base[s][k][key] is the number of items with a larger key plus n_heads * hist summed
+// over every earlier (s', k') for this key.  Kernel 1 writes hist and rank per sample;
+// kernel 2 (one workgroup per list) scans hist over keys and segments into base; kernel 3
+// places every item with one thread.
 #include "gsa_device.hpp"
 #include "gsa_internal.hpp"
 
@@ -37,28 +38,25 @@ namespace {
 
 constexpr int kMaskThreads = 1024;
 constexpr int kMaskWaves = kMaskThreads / kWave;
+static_assert(kOrderKeys >= 32 - __builtin_clz(GSA_MAX_BLOCKS) + 1, "order keys of every length fit");
 
-// Exclusive scan of one int per thread over the workgroup; returns the thread's prefix
-// and writes the total to *total.  `scratch` holds kMaskWaves ints.
-__device__ int block_exclusive_scan(int v, int *scratch, int *total) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int y = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += y;
+// Sort key of a list length: its octave, floor(log2 len) + 1 (0 for an empty list).
+// Items of one head with similar lengths then sit next to each other in the work order,
+// so the kv-blocks they share meet in one L2, while the order stays longest-first to
+// within a factor of two.
+__device__ __forceinline__ int order_key(int len) { return len <= 0 ? 0 : 32 - __clz(len); }
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
+
+// First index x in [0, n) with start[x + 1] > e, for strictly increasing start[0..n].
+__device__ __forceinline__ int find_segment(const int *start, int n, int e) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= e) lo = mid;
+    else hi = mid - 1;
   }
-  if (lane == kWave - 1) scratch[wave] = incl;
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int w2 = 0; w2 < kMaskWaves; ++w2) {
-    int s = scratch[w2];
-    if (w2 < wave) base += s;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + incl - v;
+  return lo;
 }
 
 __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
@@ -68,39 +66,44 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
     int64_t cap, int32_t *__restrict__ sched, int64_t batch) {
   __shared__ int s_prefix[GSA_MAX_BLOCKS + 1];   // # literal blocks before position i
   __shared__ int s_list[GSA_MAX_BLOCKS];         // literal block ids, ascending
-  __shared__ int s_rstart[3][GSA_MAX_BLOCKS + 1];
-  __shared__ int s_cstart[3][GSA_MAX_BLOCKS + 1];
+  __shared__ int s_start[6][GSA_MAX_BLOCKS + 1]; // row starts (k), then column starts (3 + k)
   __shared__ long long s_sum[kMaskWaves];
-  __shared__ int s_scan[kMaskWaves];
-  __shared__ int s_len[6][GSA_MAX_BLOCKS];       // row lengths (k), then column lengths (3 + k)
-  __shared__ int s_hist[6][GSA_MAX_BLOCKS + 1];
+  __shared__ int s_wave[6][kMaskWaves];
+  __shared__ int s_cnt[6][kMaskWaves][kOrderKeys];
 
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int64_t s = blockIdx.x;
-  const int ci = t < n ? c[s * n + t] : 0;
+  const bool valid = t < n;
+  // Waves holding blocks; the others only help with the list entries.
+  const int active = (n + kWave - 1) / kWave;
+  const bool busy = wave < active;
+  const int ci = valid ? c[s * n + t] : 0;
+  for (int x = t; x < 6 * kMaskWaves * kOrderKeys; x += kMaskThreads) (&s_cnt[0][0][0])[x] = 0;
 
   // Sum of c over the sample, exactly, in 64 bits.
-  long long part = ci;
+  if (busy) {
+    long long part = ci;
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
-  if (lane == 0) s_sum[wave] = part;
+    for (int off = kWave / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+    if (lane == 0) s_sum[wave] = part;
+  }
   __syncthreads();
   long long sum = 0;
-  for (int w2 = 0; w2 < kMaskWaves; ++w2) sum += s_sum[w2];
+  for (int w2 = 0; w2 < active; ++w2) sum += s_sum[w2];
 
   // l_i = [N c_i > sum c]  <=>  r_i > mean r.
-  const bool lit = t < n && (long long)n * ci > sum;
+  const bool lit = valid && (long long)n * ci > sum;
   const uint64_t bal = __ballot(lit);
-  const int below = __popcll(bal & ((1ull << lane) - 1ull));
-  if (lane == 0) s_scan[wave] = __popcll(bal);
+  const int below = __popcll(bal & lanes_below(lane));
+  if (lane == 0) s_wave[0][wave] = __popcll(bal);
   __syncthreads();
   int wave_base = 0, n_lit = 0;
-  for (int w2 = 0; w2 < kMaskWaves; ++w2) {
-    if (w2 < wave) wave_base += s_scan[w2];
-    n_lit += s_scan[w2];
+  for (int w2 = 0; w2 < active; ++w2) {
+    if (w2 < wave) wave_base += s_wave[0][w2];
+    n_lit += s_wave[0][w2];
   }
   const int rank = wave_base + below;   // literal blocks j < t
-  if (t < n) {
+  if (valid) {
     flags[s * n + t] = lit ? 1 : 0;
     s_prefix[t] = rank;
     if (lit) s_list[rank] = t;
@@ -111,194 +114,273 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
   }
   __syncthreads();
 
-  // List lengths in closed form (w >= n - 1 behaves like w = n).
+  // List lengths in closed form (w >= n - 1 behaves like w = n): rows k, columns 3 + k.
   const int ww = w < n ? w : n;
-  int rlen[3] = {0, 0, 0}, clen[3] = {0, 0, 0};
-  if (t < n) {
+  int len[6] = {0, 0, 0, 0, 0, 0};
+  if (valid) {
     const int win = (t < ww ? t : ww) + 1;
-    rlen[0] = win;
-    rlen[1] = lit ? rank + 1 : 1;
-    rlen[2] = win + (lit ? s_prefix[t - ww > 0 ? t - ww : 0] : 0);
+    len[0] = win;
+    len[1] = lit ? rank + 1 : 1;
+    len[2] = win + (lit ? s_prefix[t - ww > 0 ? t - ww : 0] : 0);
     const int after = n - 1 - t;
     const int cwin = (after < ww ? after : ww) + 1;
     const int beyond = t + ww + 1 < n ? t + ww + 1 : n;
-    clen[0] = cwin;
-    clen[1] = lit ? n_lit - rank : 1;
-    clen[2] = cwin + (lit ? n_lit - s_prefix[beyond] : 0);
-  }
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    int tot;
-    const int rs = block_exclusive_scan(rlen[k], s_scan, &tot);
-    int32_t *rp = row_ptr + (s * 3 + k) * (int64_t)(n + 1);
-    if (t < n) {
-      rp[t] = rs;
-      s_rstart[k][t] = rs;
-    }
-    if (t == 0) {
-      rp[n] = tot;
-      s_rstart[k][n] = tot;
-      n_edges[s * 3 + k] = tot;
-    }
-    const int cs = block_exclusive_scan(clen[k], s_scan, &tot);
-    int32_t *cp = col_ptr + (s * 3 + k) * (int64_t)(n + 1);
-    if (t < n) {
-      cp[t] = cs;
-      s_cstart[k][t] = cs;
-    }
-    if (t == 0) {
-      cp[n] = tot;
-      s_cstart[k][n] = tot;
-    }
-  }
-  // Per-(list, class) length histograms and stable ranks among equal lengths.
-  for (int x = t; x < 6 * (GSA_MAX_BLOCKS + 1); x += kMaskThreads) (&s_hist[0][0])[x] = 0;
-  if (t < n) {
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      s_len[k][t] = rlen[k];
-      s_len[3 + k][t] = clen[k];
-    }
-  }
-  __syncthreads();
-  if (t < n) {
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      atomicAdd(&s_hist[k][rlen[k]], 1);
-      atomicAdd(&s_hist[3 + k][clen[k]], 1);
-    }
-  }
-  int rank6[6] = {0, 0, 0, 0, 0, 0};
-  if (t < n) {
-    int mine[6];
-#pragma unroll
-    for (int q = 0; q < 6; ++q) mine[q] = s_len[q][t];
-    for (int j2 = 0; j2 < t; ++j2) {
-#pragma unroll
-      for (int q = 0; q < 6; ++q) rank6[q] += s_len[q][j2] == mine[q] ? 1 : 0;
-    }
-  }
-  __syncthreads();
-  {
-    const int seg = 3 * n + 2;
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      const int list = q / 3, k = q % 3;
-      int32_t *sg = sched + ((list * batch + s) * 3 + k) * (int64_t)seg;
-      for (int l = t; l <= n; l += kMaskThreads) sg[l] = s_hist[q][l];
-      if (t < n) sg[2 * n + 2 + t] = rank6[q];
-    }
+    len[3] = cwin;
+    len[4] = lit ? n_lit - rank : 1;
+    len[5] = cwin + (lit ? n_lit - s_prefix[beyond] : 0);
   }
 
-  // Rows: wave-per-row, lanes on consecutive entries.
+  // One exclusive scan of the six lengths, and the ranks among equal keys: lanes with the
+  // same key agree on every key bit, so AND-ing the ballots of the bits (or of their
+  // complements) gives the wave's lanes with this lane's key.
+  const uint64_t live = __ballot(valid);
+  int incl[6] = {}, key[6] = {}, in_rank[6] = {};
+  if (busy) {
+#pragma unroll
+  for (int q = 0; q < 6; ++q) {
+    incl[q] = len[q];
+    key[q] = valid ? order_key(len[q]) : 0;
+    uint64_t same = live;
+#pragma unroll
+    for (int bit = 0; bit < 4; ++bit) {
+      const bool on = (key[q] >> bit) & 1;
+      const uint64_t b = __ballot(on);
+      same &= on ? b : ~b;
+    }
+    in_rank[q] = __popcll(same & lanes_below(lane));
+    if (valid && in_rank[q] == 0) s_cnt[q][wave][key[q]] = __popcll(same);
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const int y = __shfl_up(incl[q], off, kWave);
+      if (lane >= off) incl[q] += y;
+    }
+  }
+  if (lane == kWave - 1) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) s_wave[q][wave] = incl[q];
+  }
+  }
+  __syncthreads();
+
+  // Per (list-class q, key): exclusive scan of the wave counts over waves; the total is the
+  // (s, class) histogram entry.
+  int32_t *hist = sched;
+  int32_t *packed = sched + 4 * batch * 3 * kOrderKeys;
+  if (t < 6 * kOrderKeys) {
+    const int q = t / kOrderKeys, kk = t % kOrderKeys;
+    int run = 0;
+    for (int w2 = 0; w2 < active; ++w2) {
+      const int v = s_cnt[q][w2][kk];
+      s_cnt[q][w2][kk] = run;
+      run += v;
+    }
+    hist[(((q / 3) * batch + s) * 3 + q % 3) * kOrderKeys + kk] = run;
+  }
+#pragma unroll
+  for (int q = 0; q < 6 && busy; ++q) {
+    int base = 0, tot = 0;
+    for (int w2 = 0; w2 < active; ++w2) {
+      const int v = s_wave[q][w2];
+      if (w2 < wave) base += v;
+      tot += v;
+    }
+    const int start = base + incl[q] - len[q];
+    int32_t *ptr = (q < 3 ? row_ptr : col_ptr) + (s * 3 + q % 3) * (int64_t)(n + 1);
+    if (valid) {
+      ptr[t] = start;
+      s_start[q][t] = start;
+    }
+    if (t == 0) {
+      ptr[n] = tot;
+      s_start[q][n] = tot;
+      if (q < 3) n_edges[s * 3 + q] = tot;
+    }
+  }
+  __syncthreads();
+  if (valid) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q)
+      packed[(((q / 3) * batch + s) * 3 + q % 3) * (int64_t)n + t] =
+          ((s_cnt[q][wave][key[q]] + in_rank[q]) << 4) | key[q];
+  }
+
+  // List entries, one thread each.  Row i of class k, entry e of it:
+#pragma unroll
   for (int k = 0; k < 3; ++k) {
-    int32_t *ci_out = col_idx + (s * 3 + k) * cap;
-    int32_t *ri_out = row_idx + (s * 3 + k) * cap;
-    for (int i = wave; i < n; i += kMaskWaves) {
+    int32_t *out = col_idx + (s * 3 + k) * cap;
+    const int total = s_start[k][n];
+    for (int e0 = t; e0 < total; e0 += kMaskThreads) {
+      const int i = find_segment(s_start[k], n, e0);
+      const int e = e0 - s_start[k][i];
       const int lo = i - ww > 0 ? i - ww : 0;
       const bool li = s_prefix[i + 1] != s_prefix[i];
-      const int beg = s_rstart[k][i], len = s_rstart[k][i + 1] - beg;
-      const int n_far = (k == 2 && li) ? s_prefix[lo] : 0;   // literal j < i - w
-      for (int e = lane; e < len; e += kWave) {
-        int j;
-        if (k == 0) j = lo + e;
-        else if (k == 1) j = li ? s_list[e] : i;
-        else j = e < n_far ? s_list[e] : lo + (e - n_far);
-        ci_out[beg + e] = j;
+      int j;
+      if (k == 0) {
+        j = lo + e;
+      } else if (k == 1) {
+        j = li ? s_list[e] : i;
+      } else {
+        const int n_far = li ? s_prefix[lo] : 0;   // literal j < i - w
+        j = e < n_far ? s_list[e] : lo + (e - n_far);
       }
-      // Column i (the same i, used as a kv-block index).
-      const int cbeg = s_cstart[k][i], clen2 = s_cstart[k][i + 1] - cbeg;
-      const int after = n - 1 - i;
-      const int cwin = (after < ww ? after : ww) + 1;
-      const int first_far = s_prefix[i + ww + 1 < n ? i + ww + 1 : n];
-      const int rank_i = s_prefix[i];
-      for (int e = lane; e < clen2; e += kWave) {
-        int r;
-        if (k == 0) r = i + e;
-        else if (k == 1) r = li ? s_list[rank_i + e] : i;
-        else r = e < cwin ? i + e : s_list[first_far + (e - cwin)];
-        ri_out[cbeg + e] = r;
+      out[e0] = j;
+    }
+  }
+  // Column j of class k, entry e of it:
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    int32_t *out = row_idx + (s * 3 + k) * cap;
+    const int total = s_start[3 + k][n];
+    for (int e0 = t; e0 < total; e0 += kMaskThreads) {
+      const int j = find_segment(s_start[3 + k], n, e0);
+      const int e = e0 - s_start[3 + k][j];
+      const bool lj = s_prefix[j + 1] != s_prefix[j];
+      int i;
+      if (k == 0) {
+        i = j + e;
+      } else if (k == 1) {
+        i = lj ? s_list[s_prefix[j] + e] : j;
+      } else {
+        const int after = n - 1 - j;
+        const int cwin = (after < ww ? after : ww) + 1;
+        const int first_far = s_prefix[j + ww + 1 < n ? j + ww + 1 : n];
+        i = e < cwin ? j + e : s_list[first_far + (e - cwin)];
       }
+      out[e0] = i;
     }
   }
 }
 
-constexpr int kSortThreads = 1024;
+// base[list][s][k][key] from hist: one workgroup per list.  Segments (s, k) weigh their
+// counts by the heads of class k; keys are taken largest first.
+constexpr int kOrderThreads = 256;
+constexpr int kOrderWaves = kOrderThreads / kWave;
 
-// blockIdx.x == 0 orders by CSR row length into work_row, 1 by CSC column length into
-// work_col.  See the work-order note at the top of this file.
-__global__ __launch_bounds__(kSortThreads) void worklist_kernel(
-    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_ptr, int64_t batch, int n,
-    int n_loc, int n_lit, int n_hyb, int32_t *__restrict__ sched, int32_t *__restrict__ work_row,
-    int32_t *__restrict__ work_col) {
-  __shared__ int s_scan[kSortThreads / kWave];
+// The 16 counts of segment `seg` (zeros past the end), weighted by its class's heads; four
+// 16-byte loads issued together.
+__device__ __forceinline__ void load_counts(const int32_t *hist, int64_t seg, int64_t nseg, const int *nh,
+                                            int (&v)[kOrderKeys]) {
+  static_assert(kOrderKeys == 16, "four int4 per segment");
+  u32x4 x[4] = {};
+  if (seg < nseg) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(hist + seg * kOrderKeys);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = src[u];
+  }
+  const int wgt = seg < nseg ? nh[seg % 3] : 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * u + e] = wgt * (int)x[u][e];
+}
 
+__global__ __launch_bounds__(kOrderThreads) void order_base_kernel(int64_t batch, int n_loc, int n_lit,
+                                                                   int n_hyb, int32_t *__restrict__ sched) {
+  __shared__ int s_tot[kOrderKeys][kOrderWaves], s_first[kOrderKeys], s_carry[kOrderKeys];
+  __shared__ int s_part[kOrderKeys][kOrderWaves];
   const int list = blockIdx.x;
-  const int32_t *ptr = list == 0 ? row_ptr : col_ptr;
-  int32_t *out = list == 0 ? work_row : work_col;
-  const int nh[3] = {n_loc, n_lit, n_hyb};
-  const int heads = n_loc + n_lit + n_hyb;
-  const int seg = 3 * n + 2;
-  int32_t *base_list = sched + list * batch * 3 * (int64_t)seg;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-  const int64_t nseg = batch * 3;
-
-  // Totals per length, over every sample and class, weighted by heads per class.  The
-  // (sample, class) loop is unrolled in groups so its loads are in flight together.
-  int tot = 0;
-  const int len = n - t;                 // thread t owns length n - t (bin t: longest first)
-  if (t < n) {
-    for (int64_t q0 = 0; q0 < nseg; q0 += 8) {
-      int v[8];
+  const int nh[3] = {n_loc, n_lit, n_hyb};
+  const int64_t nseg = 3 * batch;
+  const int32_t *hist = sched + list * nseg * kOrderKeys;
+  int32_t *base = sched + (2 + list) * nseg * kOrderKeys;
+  int v[kOrderKeys];
+  // Items per key over every segment (the first chunk's counts stay in registers).
+  int tot[kOrderKeys] = {};
+  for (int64_t c0 = 0; c0 < nseg; c0 += kOrderThreads) {
+    load_counts(hist, c0 + t, nseg, nh, v);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = q0 + u < nseg ? base_list[(q0 + u) * seg + len] : 0;
+    for (int kk = 0; kk < kOrderKeys; ++kk) tot[kk] += v[kk];
+  }
+  const bool any = wave * kWave < nseg;   // this wave ever holds a segment
 #pragma unroll
-      for (int u = 0; u < 8; ++u) tot += v[u] * (q0 + u < nseg ? nh[(q0 + u) % 3] : 0);
+  for (int kk = 0; kk < kOrderKeys; ++kk) {
+    int x = tot[kk];
+    if (any) {
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
     }
+    if (lane == 0) s_tot[kk][wave] = x;
   }
-  // Exclusive scan over bins (longest first) gives each length's start position.
-  int incl = tot;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int y = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += y;
-  }
-  if (lane == kWave - 1) s_scan[wave] = incl;
+  if (t < kOrderKeys) s_carry[t] = 0;
   __syncthreads();
-  int wbase = 0;
-  for (int w2 = 0; w2 < wave; ++w2) wbase += s_scan[w2];
-  int running = wbase + incl - tot;
-  // base[s][k][len]: start of the first head of class k of sample s among this length.
-  if (t < n) {
-    for (int64_t q0 = 0; q0 < nseg; q0 += 8) {
-      int v[8];
+  if (t < kOrderKeys) {
+    int first = 0;
+    for (int k2 = t + 1; k2 < kOrderKeys; ++k2)
+      for (int w2 = 0; w2 < kOrderWaves; ++w2) first += s_tot[k2][w2];
+    s_first[t] = first;
+  }
+  // Exclusive scan over segments, per key, one chunk of segments at a time.
+  for (int64_t c0 = 0; c0 < nseg; c0 += kOrderThreads) {
+    const int64_t seg = c0 + t;
+    if (c0 > 0) load_counts(hist, seg, nseg, nh, v);
+    int incl[kOrderKeys];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = q0 + u < nseg ? base_list[(q0 + u) * seg + len] : 0;
+    for (int kk = 0; kk < kOrderKeys; ++kk) incl[kk] = v[kk];
+    if (c0 + wave * kWave < nseg) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (q0 + u < nseg) {
-          base_list[(q0 + u) * seg + n + 1 + len] = running;
-          running += v[u] * nh[(q0 + u) % 3];
-        }
+    for (int off = 1; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int kk = 0; kk < kOrderKeys; ++kk) {
+        const int y = __shfl_up(incl[kk], off, kWave);
+        if (lane >= off) incl[kk] += y;
       }
     }
+    }
+    if (lane == kWave - 1) {
+#pragma unroll
+      for (int kk = 0; kk < kOrderKeys; ++kk) s_part[kk][wave] = incl[kk];
+    }
+    __syncthreads();
+    if (seg < nseg) {
+      int out[kOrderKeys];
+#pragma unroll
+      for (int kk = 0; kk < kOrderKeys; ++kk) {
+        int before = s_carry[kk];
+        for (int w2 = 0; w2 < wave; ++w2) before += s_part[kk][w2];
+        out[kk] = s_first[kk] + before + incl[kk] - v[kk];
+      }
+      u32x4 *dst = reinterpret_cast<u32x4 *>(base + seg * kOrderKeys);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dst[u] = u32x4{(uint32_t)out[4 * u], (uint32_t)out[4 * u + 1], (uint32_t)out[4 * u + 2],
+                       (uint32_t)out[4 * u + 3]};
+    }
+    __syncthreads();
+    if (t < kOrderKeys) {
+      int sum = 0;
+      for (int w2 = 0; w2 < kOrderWaves; ++w2) sum += s_part[t][w2];
+      s_carry[t] += sum;
+    }
+    __syncthreads();
   }
-  __syncthreads();
+}
 
-  // Scatter: every item computes its own position.
+// Places every item of both work lists: grid (items / 256, 2).
+__global__ __launch_bounds__(256) void order_scatter_kernel(const int32_t *__restrict__ sched, int64_t batch, int n,
+                                                            int n_loc, int n_lit, int n_hyb,
+                                                            int32_t *__restrict__ work_row,
+                                                            int32_t *__restrict__ work_col) {
+  const int heads = n_loc + n_lit + n_hyb;
   const int64_t items = batch * heads * (int64_t)n;
-  for (int64_t idx = t; idx < items; idx += kSortThreads) {
-    const int i = (int)(idx % n);
-    const int64_t sh = idx / n;
-    const int h = (int)(sh % heads);
-    const int64_t s = sh / heads;
-    const int k = h < n_loc ? 0 : (h < n_loc + n_lit ? 1 : 2);
-    const int h0 = k == 0 ? 0 : (k == 1 ? n_loc : n_loc + n_lit);
-    const int32_t *p = ptr + (s * 3 + k) * (int64_t)(n + 1);
-    const int l = p[i + 1] - p[i];
-    const int32_t *sg = base_list + (s * 3 + k) * (int64_t)seg;
-    out[sg[n + 1 + l] + (h - h0) * sg[l] + sg[2 * n + 2 + i]] = (int32_t)idx;
-  }
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= items) return;
+  const int list = blockIdx.y;
+  const int i = (int)(idx % n);
+  const int64_t sh = idx / n;
+  const int h = (int)(sh % heads);
+  const int64_t s = sh / heads;
+  const int k = h < n_loc ? 0 : (h < n_loc + n_lit ? 1 : 2);
+  const int h0 = k == 0 ? 0 : (k == 1 ? n_loc : n_loc + n_lit);
+  const int64_t seg = (list * batch + s) * 3 + k;
+  const int32_t pk = sched[4 * batch * 3 * kOrderKeys + seg * n + i];
+  const int64_t slot = seg * kOrderKeys + (pk & 15);
+  const int32_t *hist = sched;
+  const int32_t *base = sched + 2 * batch * 3 * kOrderKeys;
+  (list == 0 ? work_row : work_col)[base[slot] + (h - h0) * hist[slot] + (pk >> 4)] = (int32_t)idx;
 }
 
 }  // namespace
@@ -310,11 +392,15 @@ gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t st
                      m.n_edges, mask_cap(n), m.sched, m.batch);
   gsa_status st = check_launch("mask_kernel");
   if (st != GSA_OK) return st;
-  if (m.n_heads[0] + m.n_heads[1] + m.n_heads[2] == 0) return GSA_OK;
-  hipLaunchKernelGGL(worklist_kernel, dim3(2), dim3(kSortThreads), 0, stream, m.row_ptr, m.col_ptr,
-                     m.batch, n, m.n_heads[0], m.n_heads[1], m.n_heads[2], m.sched, m.work_row,
-                     m.work_col);
-  return check_launch("worklist_kernel");
+  const int64_t items = m.batch * (int64_t)(m.n_heads[0] + m.n_heads[1] + m.n_heads[2]) * n;
+  if (items == 0) return GSA_OK;
+  hipLaunchKernelGGL(order_base_kernel, dim3(2), dim3(kOrderThreads), 0, stream, m.batch, m.n_heads[0],
+                     m.n_heads[1], m.n_heads[2], m.sched);
+  st = check_launch("order_base_kernel");
+  if (st != GSA_OK) return st;
+  hipLaunchKernelGGL(order_scatter_kernel, dim3((unsigned)((items + 255) / 256), 2), dim3(256), 0, stream,
+                     m.sched, m.batch, n, m.n_heads[0], m.n_heads[1], m.n_heads[2], m.work_row, m.work_col);
+  return check_launch("order_scatter_kernel");
 }
 
 }  // namespace gsa

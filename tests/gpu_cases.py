@@ -26,7 +26,8 @@ def expected_mask(c: np.ndarray, block: int, window: int):
 
 
 def expected_work(masks, n_heads, by_columns: bool):
-    """Every (s, h, i) as (s*H + h)*N + i, longest list first, ties by ascending index."""
+    """Every (s, h, i) as (s*H + h)*N + i, sorted by the octave of its list length,
+    floor(log2 len) + 1, largest first, ties by ascending index."""
     classes = oracle.head_classes(n_heads)
     b, _, n, _ = masks.shape
     lengths = []
@@ -35,7 +36,8 @@ def expected_work(masks, n_heads, by_columns: bool):
             m = masks[s, classes[h]]
             lengths.append(m.sum(axis=0) if by_columns else m.sum(axis=1))
     lengths = np.concatenate(lengths) if lengths else np.zeros(0, np.int64)
-    return np.argsort(-lengths, kind="stable").astype(np.int64)
+    key = np.array([int(x).bit_length() for x in lengths], dtype=np.int64)
+    return np.argsort(-key, kind="stable").astype(np.int64)
 
 
 def check_mask(m: gsa.GsaMask, c: np.ndarray, block: int, window: int, n_heads):

@@ -75,7 +75,7 @@ def test_mask_sizes():
     sizes = gsa.gsa_mask_sizes(2, 5, (2, 1, 1))
     cap = 15
     assert sizes == [10, 8, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 8,
-                     2 * 4 * 5 * 4, 2 * 4 * 5 * 4, 2 * 3 * 2 * (3 * 5 + 2) * 4]
+                     2 * 4 * 5 * 4, 2 * 4 * 5 * 4, 2 * 3 * 2 * (5 + 32) * 4]
     with pytest.raises(gsa.GsaError):
         gsa.gsa_mask_sizes(-1, 5, (1, 1, 1))
 
@@ -83,12 +83,12 @@ def test_mask_sizes():
 FAKE = 0x10000   # a non-NULL, aligned address: validation must fail before it is used
 
 
-def _mask(batch=2, n=4, window=1, heads=(2, 1, 1), null=()):
+def _mask(batch=2, n=4, window=1, heads=(2, 1, 1), null=(), misalign=()):
     m = gsa._Mask()
     m.batch, m.n_blocks, m.window = batch, n, window
     m.n_heads[:] = list(heads)
     for f in gsa.MASK_FIELDS:
-        setattr(m, f, None if f in null else FAKE)
+        setattr(m, f, None if f in null else FAKE + (4 if f in misalign else 0))
     return m
 
 
@@ -114,6 +114,7 @@ def test_build_mask_validation(lib):
     assert lib.gsa_build_mask(FAKE, ctypes.byref(_mask(null=("col_idx",))), None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(FAKE, ctypes.byref(_mask(null=("flags",))), None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(FAKE, ctypes.byref(_mask(null=("sched",))), None) == gsa.GSA_ERR_ARG
+    assert lib.gsa_build_mask(FAKE, ctypes.byref(_mask(misalign=("sched",))), None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(None, ctypes.byref(_mask()), None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(FAKE, None, None) == gsa.GSA_ERR_ARG
     assert lib.gsa_build_mask(None, ctypes.byref(_mask(batch=0)), None) == gsa.GSA_OK
