@@ -43,6 +43,8 @@ static gsa_status check_mask(const gsa_mask *m, bool building) {
     return fail(GSA_ERR_UNSUPPORTED, "n_blocks %d outside 1..%d", m->n_blocks, GSA_MAX_BLOCKS);
   if (!m->row_ptr || !m->col_idx || !m->col_ptr || !m->row_idx || !m->work_row || !m->work_col)
     return fail(GSA_ERR_ARG, "mask list buffer is NULL");
+  if (!aligned16(m->work_row) || !aligned16(m->work_col))
+    return fail(GSA_ERR_ARG, "mask work buffers are not 16-byte aligned");
   if (building && (!m->flags || !m->n_literal || !m->n_edges || !m->sched))
     return fail(GSA_ERR_ARG, "mask flag/count/sched buffer is NULL");
   if (building && !aligned16(m->sched)) return fail(GSA_ERR_ARG, "mask sched buffer is not 16-byte aligned");
@@ -120,8 +122,8 @@ gsa_status gsa_mask_sizes(int64_t batch, int32_t n_blocks, const int32_t n_heads
   sizes_out[4] = B * 3 * (N + 1) * 4;        // col_ptr
   sizes_out[5] = B * 3 * cap * 4;            // row_idx
   sizes_out[6] = B * 3 * 8;                  // n_edges
-  sizes_out[7] = B * H * N * 4;              // work_row
-  sizes_out[8] = B * H * N * 4;              // work_col
+  sizes_out[7] = B * H * N * 16;             // work_row: 4 int32 per item
+  sizes_out[8] = B * H * N * 16;             // work_col
   sizes_out[9] = (size_t)sched_words(batch, n_blocks) * 4;  // sched: work-order scratch
   return GSA_OK;
 }

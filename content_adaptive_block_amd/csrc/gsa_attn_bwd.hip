@@ -345,7 +345,7 @@ gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStre
     if (st != GSA_OK) return st;
   }
   if (stages & kBwdDq) {
-    const WorkLists wl{m.work_row, m.row_ptr, m.col_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
+    const WorkLists wl{m.work_row, m.col_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
                        mask_cap(m.n_blocks)};
     hipLaunchKernelGGL((bwd_dq_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream, q, k, v,
                        o, dout, f.lse, a.workspace, static_cast<T *>(a.dq), wl, sl2, scale);
@@ -353,7 +353,7 @@ gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStre
     if (st != GSA_OK) return st;
   }
   if (stages & kBwdDkdv) {
-    const WorkLists wl{m.work_col, m.col_ptr, m.row_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
+    const WorkLists wl{m.work_col, m.row_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
                        mask_cap(m.n_blocks)};
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(SK::kThreads), 0, stream, q, k,
                        v, dout, f.lse, a.workspace, static_cast<T *>(a.dk), static_cast<T *>(a.dv), wl, sl2,

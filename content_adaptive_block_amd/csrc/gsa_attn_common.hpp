@@ -36,32 +36,35 @@ __device__ __forceinline__ int head_class(int h, int n_loc, int n_lit) {
   return h < n_loc ? 0 : (h < n_loc + n_lit ? 1 : 2);
 }
 
-// One work item: list `list[beg, end)` of block `blk` of head `sh` = s * H + h.
+// One work item: list `list[beg, end)` of block `blk` of head `sh` = s * H + h; `first`
+// is list[beg].
 struct WorkItem {
   int64_t sh;
-  int blk, beg, end;
+  int blk, beg, end, first;
   const int32_t *list;
 };
 
-// Where work items live: the work list (item indices (s*H + h)*N + blk) and the
-// per-(sample, class) list pointers (CSR rows or CSC columns).
+// Where work items live: the work descriptors (item index (s*H + h)*N + blk, beg, end,
+// first entry) in schedule order, and the per-(sample, class) lists (CSR rows or CSC
+// columns).  One 16-byte load describes an item, so the first tile copy waits on a single
+// memory access.
 struct WorkLists {
-  const int32_t *work, *ptr, *idx;
+  const int32_t *work, *idx;
   int heads, n, n_loc, n_lit;
   int64_t cap;
   __device__ __forceinline__ WorkItem decode(int64_t pos) const {
-    const uint32_t item = (uint32_t)work[pos];
+    const u32x4 d = reinterpret_cast<const u32x4 *>(work)[pos];
     WorkItem it;
+    const uint32_t item = d[0];
     it.blk = (int)(item % (uint32_t)n);
     const uint32_t sh = item / (uint32_t)n;
     it.sh = sh;
     const int h = (int)(sh % (uint32_t)heads);
     const int64_t s = sh / (uint32_t)heads;
-    const int cls = head_class(h, n_loc, n_lit);
-    const int32_t *p = ptr + (s * 3 + cls) * (int64_t)(n + 1);
-    it.list = idx + (s * 3 + cls) * cap;
-    it.beg = p[it.blk];
-    it.end = p[it.blk + 1];
+    it.list = idx + (s * 3 + head_class(h, n_loc, n_lit)) * cap;
+    it.beg = (int)d[1];
+    it.end = (int)d[2];
+    it.first = (int)d[3];
     return it;
   }
 };
@@ -286,14 +289,23 @@ struct AttnShape {
 // ---------------------------------------------------------------------------------------
 template <class P>
 __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
+  // Entries after the first come from a lane-indexed register holding 64 of them (one
+  // per lane), read with readlane: no step waits on memory for its next kv index.
+  const int lane = threadIdx.x & (kWave - 1);
+  int chunk = it.beg + 1 + lane < it.end ? it.list[it.beg + 1 + lane] : 0;
   pol.operands(it);
-  pol.copy(it, it.list[it.beg], 0);
+  pol.copy(it, it.first, 0);
   pol.begin(it);
   int stage = 0;
   for (int e = it.beg; e < it.end; ++e) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    if (e + 1 < it.end) pol.copy(it, it.list[e + 1], stage ^ 1);
+    const int nx = e + 1 - (it.beg + 1);   // position of entry e + 1 after the first
+    if (e + 1 < it.end) {
+      if (nx > 0 && (nx & (kWave - 1)) == 0)
+        chunk = e + 1 + lane < it.end ? it.list[e + 1 + lane] : 0;
+      pol.copy(it, __builtin_amdgcn_readlane(chunk, nx & (kWave - 1)), stage ^ 1);
+    }
     pol.compute(it, e, stage);
     stage ^= 1;
   }

@@ -145,7 +145,7 @@ gsa_status launch_fwd_instance(const gsa_fwd_args &a, const gsa_mask &m, hipStre
   const int64_t items = a.batch * a.heads * (int64_t)m.n_blocks;
   const float scale = a.scale > 0.f ? a.scale : 1.0f / sqrtf((float)HD);
   const float sl2 = scale * 1.4426950408889634f;
-  const WorkLists wl{m.work_row, m.row_ptr, m.col_idx, a.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
+  const WorkLists wl{m.work_row, m.col_idx, a.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
                      mask_cap(m.n_blocks)};
   hipLaunchKernelGGL((attn_fwd_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),

@@ -29,7 +29,8 @@
 // and base[s][k][key] is the number of items with a larger key plus n_heads * hist summed
 // over every earlier (s', k') for this key.  Kernel 1 writes hist and rank per sample;
 // kernel 2 (one workgroup per list) scans hist over keys and segments into base; kernel 3
-// places every item with one thread.
+// places every item with one thread, as a descriptor (item, beg, end, first entry) that
+// the attention kernels read with one load.
 #include "gsa_device.hpp"
 #include "gsa_internal.hpp"
 
@@ -359,9 +360,14 @@ __global__ __launch_bounds__(kOrderThreads) void order_base_kernel(int64_t batch
   }
 }
 
-// Places every item of both work lists: grid (items / 256, 2).
+// Places every item of both work lists with its descriptor (item, beg, end, first entry):
+// grid (items / 256, 2).
 __global__ __launch_bounds__(256) void order_scatter_kernel(const int32_t *__restrict__ sched, int64_t batch, int n,
                                                             int n_loc, int n_lit, int n_hyb,
+                                                            const int32_t *__restrict__ row_ptr,
+                                                            const int32_t *__restrict__ col_idx,
+                                                            const int32_t *__restrict__ col_ptr,
+                                                            const int32_t *__restrict__ row_idx, int64_t cap,
                                                             int32_t *__restrict__ work_row,
                                                             int32_t *__restrict__ work_col) {
   const int heads = n_loc + n_lit + n_hyb;
@@ -377,10 +383,15 @@ __global__ __launch_bounds__(256) void order_scatter_kernel(const int32_t *__res
   const int h0 = k == 0 ? 0 : (k == 1 ? n_loc : n_loc + n_lit);
   const int64_t seg = (list * batch + s) * 3 + k;
   const int32_t pk = sched[4 * batch * 3 * kOrderKeys + seg * n + i];
+  const int32_t *ptr = (list == 0 ? row_ptr : col_ptr) + (s * 3 + k) * (int64_t)(n + 1);
+  const int beg = ptr[i], end = ptr[i + 1];
+  const int first = (list == 0 ? col_idx : row_idx)[(s * 3 + k) * cap + beg];
   const int64_t slot = seg * kOrderKeys + (pk & 15);
   const int32_t *hist = sched;
   const int32_t *base = sched + 2 * batch * 3 * kOrderKeys;
-  (list == 0 ? work_row : work_col)[base[slot] + (h - h0) * hist[slot] + (pk >> 4)] = (int32_t)idx;
+  const int64_t pos = base[slot] + (h - h0) * hist[slot] + (pk >> 4);
+  reinterpret_cast<u32x4 *>(list == 0 ? work_row : work_col)[pos] =
+      u32x4{(uint32_t)idx, (uint32_t)beg, (uint32_t)end, (uint32_t)first};
 }
 
 }  // namespace
@@ -399,7 +410,8 @@ gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t st
   st = check_launch("order_base_kernel");
   if (st != GSA_OK) return st;
   hipLaunchKernelGGL(order_scatter_kernel, dim3((unsigned)((items + 255) / 256), 2), dim3(256), 0, stream,
-                     m.sched, m.batch, n, m.n_heads[0], m.n_heads[1], m.n_heads[2], m.work_row, m.work_col);
+                     m.sched, m.batch, n, m.n_heads[0], m.n_heads[1], m.n_heads[2], m.row_ptr, m.col_idx,
+                     m.col_ptr, m.row_idx, mask_cap(n), m.work_row, m.work_col);
   return check_launch("order_scatter_kernel");
 }
 

@@ -102,11 +102,14 @@ gsa_status gsa_prepare(const uint8_t *bytes, int64_t batch, int64_t seq_len, int
  *   col_ptr   int32 [B, 3, N + 1]     CSC offsets into row_idx's (s, class) segment
  *   row_idx   int32 [B, 3, cap]       query blocks i keeping kv-block j, ascending
  *   n_edges   int64 [B, 3]            kept block pairs per (sample, class)
- *   work_row  int32 [B * H * N]       every (s, h, i) as (s*H + h)*N + i, sorted by the
- *                                     octave floor(log2 len) + 1 of its CSR row length,
- *                                     largest first, ties in ascending index (forward and
- *                                     dQ order)
- *   work_col  int32 [B * H * N]       the same over CSC column lengths (dK/dV order)
+ *   work_row  int32 [B * H * N, 4]    one descriptor per (s, h, i), in schedule order:
+ *                                     (item (s*H + h)*N + i, beg, end, first), where
+ *                                     [beg, end) is row i's range in col_idx's (s, class)
+ *                                     segment and first = its first entry; sorted by the
+ *                                     octave floor(log2 len) + 1 of the row length
+ *                                     len = end - beg, largest first, ties in ascending
+ *                                     item (forward and dQ order); 16-byte aligned
+ *   work_col  int32 [B * H * N, 4]    the same over CSC columns and row_idx (dK/dV order)
  *   sched     int32 [2*3*B*(N+32)]    scratch of the work-order construction, 16-byte
  *                                     aligned (contents unspecified after the call)
  * Entries of col_idx/row_idx past a segment's total are left untouched.

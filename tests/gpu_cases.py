@@ -62,8 +62,17 @@ def check_mask(m: gsa.GsaMask, c: np.ndarray, block: int, window: int, n_heads):
             assert np.array_equal(row_idx[s, k, :cp[-1]], ri), (s, k)
             assert n_edges[s, k] == masks[s, k].sum()
     if sum(n_heads):
-        assert np.array_equal(m.work_row.cpu().numpy(), expected_work(masks, n_heads, False))
-        assert np.array_equal(m.work_col.cpu().numpy(), expected_work(masks, n_heads, True))
+        heads = sum(n_heads)
+        classes = oracle.head_classes(n_heads)
+        for name, by_cols, ptr, idx in (("work_row", False, row_ptr, col_idx), ("work_col", True, col_ptr, row_idx)):
+            desc = getattr(m, name).cpu().numpy().reshape(-1, 4)
+            order = expected_work(masks, n_heads, by_cols)
+            assert np.array_equal(desc[:, 0], order), name
+            s_, h_, i_ = order // (heads * n), (order // n) % heads, order % n
+            k_ = np.asarray(classes)[h_]
+            assert np.array_equal(desc[:, 1], ptr[s_, k_, i_]), name
+            assert np.array_equal(desc[:, 2], ptr[s_, k_, i_ + 1]), name
+            assert np.array_equal(desc[:, 3], idx[s_, k_, desc[:, 1]]), name
     return masks
 
 

@@ -75,7 +75,7 @@ def test_mask_sizes():
     sizes = gsa.gsa_mask_sizes(2, 5, (2, 1, 1))
     cap = 15
     assert sizes == [10, 8, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 8,
-                     2 * 4 * 5 * 4, 2 * 4 * 5 * 4, 2 * 3 * 2 * (5 + 32) * 4]
+                     2 * 4 * 5 * 16, 2 * 4 * 5 * 16, 2 * 3 * 2 * (5 + 32) * 4]
     with pytest.raises(gsa.GsaError):
         gsa.gsa_mask_sizes(-1, 5, (1, 1, 1))
 
@@ -137,6 +137,7 @@ def test_attn_fwd_validation(lib):
     assert _call_fwd(lib, _fwd(scale=-1.0), m) == gsa.GSA_ERR_ARG
     assert _call_fwd(lib, _fwd(block=0), m) == gsa.GSA_ERR_ARG
     assert _call_fwd(lib, _fwd(), _mask(null=("work_row",))) == gsa.GSA_ERR_ARG
+    assert _call_fwd(lib, _fwd(), _mask(misalign=("work_row",))) == gsa.GSA_ERR_ARG
     assert lib.gsa_attn_fwd(None, ctypes.byref(m), None) == gsa.GSA_ERR_ARG
     # empty work is a no-op
     assert _call_fwd(lib, _fwd(batch=0, null=("q", "k", "v", "o", "lse")), _mask(batch=0)) == gsa.GSA_OK
