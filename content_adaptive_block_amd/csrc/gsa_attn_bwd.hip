@@ -134,13 +134,8 @@ struct DkdvPolicy {
       for (int t = 0; t < S::kPartTiles; ++t) {
         const int qb = part * S::kPartTiles + t;
         f32x4 st[R], dp[R];
-        if constexpr (R == 2) {
-          S::dot_rows2(lq, qb * 16 + c, g, kf[0], kf[1], st[0], st[1]);
-          S::dot_rows2(ldo, qb * 16 + c, g, vf[0], vf[1], dp[0], dp[1]);
-        } else {
-          st[0] = S::dot_rows(lq, qb * 16 + c, g, kf[0]);
-          dp[0] = S::dot_rows(ldo, qb * 16 + c, g, vf[0]);
-        }
+        S::template dot_rows_n<R>(lq, qb * 16 + c, g, kf, st);
+        S::template dot_rows_n<R>(ldo, qb * 16 + c, g, vf, dp);
         const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ll + qb * 16 + 4 * g);
         const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ld + qb * 16 + 4 * g);
 #pragma unroll
@@ -153,13 +148,8 @@ struct DkdvPolicy {
             ds[kg][t][r] = pr * (dp[kg][r] - d4[r]);
           }
       }
-      if constexpr (R == 2) {
-        S::accumulate_part2(dv_acc[0], dv_acc[1], ldo, p[0], p[1], part, c, g);
-        S::accumulate_part2(dk_acc[0], dk_acc[1], lq, ds[0], ds[1], part, c, g);
-      } else {
-        S::accumulate_part(dv_acc[0], ldo, p[0], part, c, g);
-        S::accumulate_part(dk_acc[0], lq, ds[0], part, c, g);
-      }
+      S::template accumulate_part_n<R>(&dv_acc[0][0], ldo, &p[0][0], S::kPartTiles, part, c, g);
+      S::template accumulate_part_n<R>(&dk_acc[0][0], lq, &ds[0][0], S::kPartTiles, part, c, g);
     }
   }
   __device__ void finish(const Item &it) {

@@ -169,18 +169,23 @@ struct AttnShape {
     return acc;
   }
 
-  // Two C tiles of the same 16 staged rows against two fragments: one LDS read per K-step
-  // feeds both products.
-  __device__ static __forceinline__ void dot_rows2(const unsigned char *lds, int row, int g, const QFrag &f0,
-                                                   const QFrag &f1, f32x4 &c0, f32x4 &c1) {
-    c0 = f32x4{0.f, 0.f, 0.f, 0.f};
-    c1 = f32x4{0.f, 0.f, 0.f, 0.f};
-    static_assert(kBf16, "bf16 only");
+  // N C tiles of the same 16 staged rows against N fragments f[0..N): one LDS read per
+  // K-step feeds all N products.
+  template <int N>
+  __device__ static __forceinline__ void dot_rows_n(const unsigned char *lds, int row, int g, const QFrag *f,
+                                                    f32x4 *c) {
+    if constexpr (N == 1) {
+      c[0] = dot_rows(lds, row, g, f[0]);
+    } else {
+      static_assert(kBf16, "several fragments per read: bf16 only");
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lds + chunk_off(row, 4 * ks + g));
-      c0 = mfma_bf16(a, f0.f[ks], c0);
-      c1 = mfma_bf16(a, f1.f[ks], c1);
+      for (int n = 0; n < N; ++n) c[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lds + chunk_off(row, 4 * ks + g));
+#pragma unroll
+        for (int n = 0; n < N; ++n) c[n] = mfma_bf16(a, f[n].f[ks], c[n]);
+      }
     }
   }
 
@@ -227,31 +232,36 @@ struct AttnShape {
     }
   }
 
-  // accumulate_part for two C operands sharing the transposed LDS reads.
-  __device__ static __forceinline__ void accumulate_part2(f32x4 *acc0, f32x4 *acc1, const unsigned char *lds,
-                                                           const f32x4 *cm0, const f32x4 *cm1, int part, int c,
-                                                           int g) {
-    static_assert(kBf16, "bf16 only");
-    const int row0 = 32 * part + 4 * g + (c >> 2), row1 = row0 + 16;
-    const int fq = 4 * (c & 3);
-    bf16x8 b0, b1;
+  // accumulate_part for N operands sharing the transposed LDS reads: acc + n * kDB and
+  // cm + n * cm_stride are operand n's accumulators and C tiles.
+  template <int N>
+  __device__ static __forceinline__ void accumulate_part_n(f32x4 *acc, const unsigned char *lds, const f32x4 *cm,
+                                                           int cm_stride, int part, int c, int g) {
+    if constexpr (N == 1) {
+      accumulate_part(acc, lds, cm, part, c, g);
+    } else {
+      static_assert(kBf16, "several operands per read: bf16 only");
+      const int row0 = 32 * part + 4 * g + (c >> 2), row1 = row0 + 16;
+      const int fq = 4 * (c & 3);
+      bf16x8 b[N];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      b0[r] = to_bf16(cm0[0][r]);
-      b0[4 + r] = to_bf16(cm0[1][r]);
-      b1[r] = to_bf16(cm1[0][r]);
-      b1[4 + r] = to_bf16(cm1[1][r]);
-    }
+      for (int n = 0; n < N; ++n)
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      const int f = db * 16 + fq;
-      const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4 *)(lds + chunk_off(row0, f >> 3) + 2 * (f & 7)));
-      const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4 *)(lds + chunk_off(row1, f >> 3) + 2 * (f & 7)));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc0[db] = mfma_bf16(a, b0, acc0[db]);
-      acc1[db] = mfma_bf16(a, b1, acc1[db]);
+        for (int r = 0; r < 4; ++r) {
+          b[n][r] = to_bf16(cm[n * cm_stride][r]);
+          b[n][4 + r] = to_bf16(cm[n * cm_stride + 1][r]);
+        }
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int f = db * 16 + fq;
+        const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(lds + chunk_off(row0, f >> 3) + 2 * (f & 7)));
+        const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(lds + chunk_off(row1, f >> 3) + 2 * (f & 7)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int n = 0; n < N; ++n) acc[n * kDB + db] = mfma_bf16(a, b[n], acc[n * kDB + db]);
+      }
     }
   }
 
@@ -308,6 +318,54 @@ __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
     }
     pol.compute(it, e, stage);
     stage ^= 1;
+  }
+  pol.finish(it);
+}
+
+
+// ---------------------------------------------------------------------------------------
+// Three-slot pipeline for items whose two streamed tiles (K_j and V_j) are used one after
+// the other: 3 tiles of LDS instead of 4, which lets 5 rather than 4 workgroups share a
+// CU (gfx950 fits five 24 KiB workgroups but only four 32 KiB ones).  Per step e:
+//   wait for K_e and V_e, barrier (everyone left step e - 1, so the spare slot is free);
+//   copy K_{e+1} into the spare slot; compute_a (reads K_e, and V_e if it wants);
+//   barrier (everyone is done with the slot the policy frees: K_e when kFreeK, else V_e);
+//   copy V_{e+1} into it; compute_b.
+// The policy supplies operands/begin/finish as for run_item, plus
+//   copy_k(item, j, slot), copy_v(item, j, slot), compute_a(item, e, k_slot, v_slot),
+//   compute_b(item, e, k_slot, v_slot) and the constant kFreeK.
+// ---------------------------------------------------------------------------------------
+template <class P>
+__device__ __forceinline__ void run_item_ring(P &pol, const WorkItem &it) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int chunk = it.beg + 1 + lane < it.end ? it.list[it.beg + 1 + lane] : 0;
+  pol.operands(it);
+  int ks = 0, vs = 1, spare = 2;
+  pol.copy_k(it, it.first, ks);
+  pol.copy_v(it, it.first, vs);
+  pol.begin(it);
+  for (int e = it.beg; e < it.end; ++e) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    const int nx_pos = e - it.beg;   // entry e + 1 sits at this position of the chunk run
+    const bool more = e + 1 < it.end;
+    int j_next = 0;
+    if (more) {
+      if (nx_pos > 0 && (nx_pos & (kWave - 1)) == 0)
+        chunk = e + 1 + lane < it.end ? it.list[e + 1 + lane] : 0;
+      j_next = __builtin_amdgcn_readlane(chunk, nx_pos & (kWave - 1));
+      pol.copy_k(it, j_next, spare);
+    }
+    pol.compute_a(it, e, ks, vs);
+    __syncthreads();
+    const int freed = P::kFreeK ? ks : vs;
+    if (more) pol.copy_v(it, j_next, freed);
+    pol.compute_b(it, e, ks, vs);
+    // K_{e+1} sits in the spare slot and V_{e+1} in the freed one; the other is spare.
+    const int next_spare = P::kFreeK ? vs : ks;
+    ks = spare;
+    vs = freed;
+    spare = next_spare;
   }
   pol.finish(it);
 }

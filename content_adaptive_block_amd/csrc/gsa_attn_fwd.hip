@@ -7,13 +7,16 @@
 // diagonal block.  Keys outside the kept blocks carry exactly zero weight in the dense
 // masked form, so visiting only the kept blocks gives the same result.
 //
-// Design (one workgroup of BLK/16 waves per (sample, head, query block); each wave owns
-// 16 of its query rows):
+// Design (one workgroup per (sample, head, query block); each wave owns 16 or 32 of its
+// query rows):
 //   * The query rows of a wave stay in registers as the B operand of S^T = K Q^T, so
 //     each lane owns one query column of every score tile and its online-softmax state
 //     (running max m and a lane-partial sum l); the row max needs two permlane swaps.
-//   * K_j and V_j stream row-major (swizzled) into two LDS stages by asynchronous
-//     global -> LDS copies, one kept block ahead of the one being computed.  O^T =
+//     With two 16-row groups per wave (a build option) every K and V read from LDS feeds
+//     two products.
+//   * K_j and V_j stream row-major (swizzled) into a ring of three LDS tiles by
+//     asynchronous global -> LDS copies: K_{j+1} lands in the spare tile while block j
+//     is computed, V_{j+1} in K_j's tile once the scores of block j are done.  O^T =
 //     V^T P^T reads V^T with transposing LDS loads and takes P straight from the S^T
 //     accumulator (rounded to bf16 in the bf16 instance).
 //   * Scores are scaled by scale * log2(e) so every exponential is one exp2.  The
@@ -32,98 +35,131 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 
+#ifndef GSA_FWD_GROUPS
+#define GSA_FWD_GROUPS 1
+#endif
+// 16-row query groups per wave (GSA_FWD_GROUPS, bf16 at head_dim 64 only).  Two groups
+// halve the LDS reads per tile but need 146 VGPRs, which halves the resident waves; on
+// gfx950 at 8 x 8 KiB that measured slower (147 vs 135 us), so one group is the default.
 template <typename T, int BLK, int HD>
-struct FwdPolicy {
-  using S = AttnShape<T, BLK, HD>;
-  using Item = WorkItem;
-  static constexpr int kStageBytes = 2 * S::kTileBytes;
+constexpr int fwd_groups() {
+  return std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0 ? GSA_FWD_GROUPS : 1;
+}
 
-  WorkLists wl;
+template <typename T, int BLK, int HD, int R>
+struct FwdPolicy {
+  using S = AttnShape<T, BLK, HD, R>;
+  using Item = WorkItem;
+  static constexpr int kLdsBytes = 3 * S::kTileBytes;
+
   const T *q, *k, *v;
   T *o;
   float *lse;
   int64_t seq;
   float sl2;
   unsigned char *lds;
-  int tid, c, g, q_in_blk;
+  int tid, c, g, q0;   // q0: this lane's query of group 0 in the block; group r: q0 + 16 r
 
-  typename S::QFrag qf;
-  f32x4 acc[S::kDB];
-  float m_run, l_part;
+  typename S::QFrag qf[R];
+  f32x4 acc[R][S::kDB];
+  float m_run[R], l_part[R];
 
   __device__ void operands(const Item &it) {
-    S::load_row_frag(qf, q + (it.sh * seq + (int64_t)it.blk * BLK + q_in_blk) * HD, g);
+    const int64_t row0 = it.sh * seq + (int64_t)it.blk * BLK + q0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) S::load_row_frag(qf[r], q + (row0 + 16 * r) * HD, g);
   }
   __device__ void begin(const Item &) {
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run = -INFINITY;
-    l_part = 0.f;
-  }
-  __device__ void copy(const Item &it, int j, int stage) {
-    const int64_t off = (it.sh * seq + (int64_t)j * BLK) * HD;
-    unsigned char *dst = lds + stage * kStageBytes;
-    S::copy_tile(dst, k + off, tid);
-    S::copy_tile(dst + S::kTileBytes, v + off, tid);
-  }
-  __device__ void compute(const Item &it, int e, int stage) {
-    const unsigned char *lk = lds + stage * kStageBytes;
-    const unsigned char *lv = lk + S::kTileBytes;
-    // S^T tile: lane holds keys kb*16 + 4g + r of query q_in_blk.
-    f32x4 st[S::kKB];
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
-    for (int kb = 0; kb < S::kKB; ++kb) st[kb] = S::dot_rows(lk, kb * 16 + c, g, qf);
+      for (int db = 0; db < S::kDB; ++db) acc[r][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run[r] = -INFINITY;
+      l_part[r] = 0.f;
+    }
+  }
+  static constexpr bool kFreeK = true;   // K_j is done once the scores are
+  __device__ void copy_k(const Item &it, int j, int slot) {
+    S::copy_tile(lds + slot * S::kTileBytes, k + (it.sh * seq + (int64_t)j * BLK) * HD, tid);
+  }
+  __device__ void copy_v(const Item &it, int j, int slot) {
+    S::copy_tile(lds + slot * S::kTileBytes, v + (it.sh * seq + (int64_t)j * BLK) * HD, tid);
+  }
+  // S^T tiles: lane holds keys kb*16 + 4g + rr of query q0 + 16 r.
+  f32x4 st[R][S::kKB];
+  __device__ void compute_a(const Item &it, int e, int k_slot, int) {
+    const unsigned char *lk = lds + k_slot * S::kTileBytes;
+#pragma unroll
+    for (int kb = 0; kb < S::kKB; ++kb) {
+      f32x4 t[R];
+      S::template dot_rows_n<R>(lk, kb * 16 + c, g, qf, t);
+#pragma unroll
+      for (int r = 0; r < R; ++r) st[r][kb] = t[r];
+    }
     if (e == it.end - 1) {   // the diagonal block is the last (largest) entry of row i
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int kb = 0; kb < S::kKB; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (kb * 16 + 4 * g + rr > q0 + 16 * r) st[r][kb][rr] = -INFINITY;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kb * 16 + 4 * g + r > q_in_blk) st[kb][r] = -INFINITY;
-    }
-    float mx = -INFINITY;
+        for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, st[r][kb][rr]);
+      mx = group_max4(mx) * sl2;
+      if (mx > m_run[r] + kRescaleSlack) {
+        const float alpha = fast_exp2(m_run[r] - mx);
+        m_run[r] = mx;
+        l_part[r] *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < S::kKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kb][r]);
-    mx = group_max4(mx) * sl2;
-    if (mx > m_run + kRescaleSlack) {
-      const float alpha = fast_exp2(m_run - mx);
-      m_run = mx;
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < S::kDB; ++db) acc[db] *= alpha;
-    }
-#pragma unroll
-    for (int kb = 0; kb < S::kKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(fmaf(st[kb][r], sl2, -m_run));
-        st[kb][r] = p;
-        l_part += p;
+        for (int db = 0; db < S::kDB; ++db) acc[r][db] *= alpha;
       }
-    S::accumulate_pv(acc, lv, st, c, g);
+#pragma unroll
+      for (int kb = 0; kb < S::kKB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float p = fast_exp2(fmaf(st[r][kb][rr], sl2, -m_run[r]));
+          st[r][kb][rr] = p;
+          l_part[r] += p;
+        }
+    }
+  }
+  __device__ void compute_b(const Item &, int, int, int v_slot) {
+    const unsigned char *lv = lds + v_slot * S::kTileBytes;
+#pragma unroll
+    for (int part = 0; part < S::kParts; ++part)
+      S::template accumulate_part_n<R>(&acc[0][0], lv, &st[0][part * S::kPartTiles], S::kKB, part, c, g);
   }
   __device__ void finish(const Item &it) {
-    const float l = group_sum4(l_part);
-    const float inv = 1.0f / l;
-    const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk;
-    T *orow = o + q_row * HD;
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) S::store4(orow + db * 16 + 4 * g, acc[db] * inv);
-    if (lse != nullptr && g == 0) lse[q_row] = (m_run + __log2f(l)) * 0.69314718055994531f;
+    for (int r = 0; r < R; ++r) {
+      const float l = group_sum4(l_part[r]);
+      const float inv = 1.0f / l;
+      const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q0 + 16 * r;
+      T *orow = o + q_row * HD;
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db) S::store4(orow + db * 16 + 4 * g, acc[r][db] * inv);
+      if (lse != nullptr && g == 0) lse[q_row] = (m_run[r] + __log2f(l)) * 0.69314718055994531f;
+    }
   }
 };
 
 template <typename T, int BLK, int HD>
-__global__ __launch_bounds__(BLK / 16 * 64) void attn_fwd_kernel(
+__global__ __launch_bounds__((BLK / (16 * fwd_groups<T, BLK, HD>()) * 64)) void attn_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
     float *__restrict__ lse, WorkLists wl, float sl2) {
-  using P = FwdPolicy<T, BLK, HD>;
-  __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
+  constexpr int R = fwd_groups<T, BLK, HD>();
+  using P = FwdPolicy<T, BLK, HD, R>;
+  __shared__ __align__(16) unsigned char lds[P::kLdsBytes];
   const WorkItem it = wl.decode(dispatch_position(blockIdx.x, gridDim.x));
 
   P pol;
-  pol.wl = wl;
   pol.q = q;
   pol.k = k;
   pol.v = v;
@@ -135,13 +171,13 @@ __global__ __launch_bounds__(BLK / 16 * 64) void attn_fwd_kernel(
   pol.tid = threadIdx.x;
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
-  pol.q_in_blk = (threadIdx.x >> 6) * 16 + pol.c;
-  run_item(pol, it);
+  pol.q0 = (threadIdx.x >> 6) * 16 * R + pol.c;
+  run_item_ring(pol, it);
 }
 
 template <typename T, int BLK, int HD>
 gsa_status launch_fwd_instance(const gsa_fwd_args &a, const gsa_mask &m, hipStream_t stream) {
-  using S = AttnShape<T, BLK, HD>;
+  using S = AttnShape<T, BLK, HD, fwd_groups<T, BLK, HD>()>;
   const int64_t items = a.batch * a.heads * (int64_t)m.n_blocks;
   const float scale = a.scale > 0.f ? a.scale : 1.0f / sqrtf((float)HD);
   const float sl2 = scale * 1.4426950408889634f;
