@@ -194,6 +194,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5); 4 is the headline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0: skip)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps timed one by one after a 512 MiB cache flush (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain elementwise copy of this many MiB 3 times (HBM counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -287,6 +289,24 @@ def main():
             per[nm].append(ev[i].elapsed_time(ev[i + 1]))
     kern_ms = {nm: float(np.mean(v)) for nm, v in per.items()}
 
+    # Cold-cache steps: a 512 MiB write (more than the 256 MB MALL) before each step,
+    # outside the events that time it.
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+        cold_ms = []
+        for _ in range(args.cold_steps):
+            flush.fill_(1.0)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+            step(ev)
+            torch.cuda.synchronize()
+            cold_ms.append([ev[i].elapsed_time(ev[i + 1]) for i in range(n_ev - 1)])
+        del flush
+        cold_arr = np.array(cold_ms)
+        cold = {"steps": args.cold_steps, "ms_per_step": round(float(np.median(cold_arr.sum(axis=1))), 4),
+                "kernels_ms": {nm: round(float(np.median(cold_arr[:, i])), 4)
+                               for i, nm in enumerate(KERNELS[:n_ev - 1])}}
+
     n_edges = mask.n_edges.cpu().numpy().reshape(wl.batch, 3)
     n_lit = mask.n_literal.cpu().numpy()[:wl.batch]
     tiles = kept_tiles(n_edges, wl.n_heads)
@@ -332,7 +352,7 @@ def main():
         "token_exact_tflops": round((4 + (10 if wl.backward else 0)) * wl.head_dim * tok / (ms_step * 1e-3) / 1e12, 3),
         "kept_tiles": tiles, "literal_blocks": n_lit.tolist(),
         "host_prepare_ms": {"all_cores": round(prep_ms, 3), "one_thread": round(prep1_ms, 3)},
-        "kernels": kernels, "roofline": roof,
+        "kernels": kernels, "roofline": roof, "cold": cold,
     }
     if args.cpu_budget > 0:
         rec["cpu_baseline"] = cpu_baseline(wl, x, host_t, None, args.cpu_budget)
