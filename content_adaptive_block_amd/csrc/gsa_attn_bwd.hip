@@ -133,11 +133,11 @@ struct DkdvPolicy {
 #pragma unroll
       for (int t = 0; t < S::kPartTiles; ++t) {
         const int qb = part * S::kPartTiles + t;
-        f32x4 st[R], dp[R];
-        S::template dot_rows_n<R>(lq, qb * 16 + c, g, kf, st);
-        S::template dot_rows_n<R>(ldo, qb * 16 + c, g, vf, dp);
         const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ll + qb * 16 + 4 * g);
         const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ld + qb * 16 + 4 * g);
+        f32x4 st[R], dpd[R];   // dpd = dP - D: the product starts from -D
+        S::template dot_rows_n<R>(lq, qb * 16 + c, g, kf, st);
+        S::template dot_rows_n<R>(ldo, qb * 16 + c, g, vf, dpd, -d4);
 #pragma unroll
         for (int kg = 0; kg < R; ++kg)
 #pragma unroll
@@ -145,7 +145,7 @@ struct DkdvPolicy {
             float pr = fast_exp2(fmaf(st[kg][r], sl2, -l4[r] * kLog2e));
             if (diag && key0 + 16 * kg > qb * 16 + 4 * g + r) pr = 0.f;
             p[kg][t][r] = pr;
-            ds[kg][t][r] = pr * (dp[kg][r] - d4[r]);
+            ds[kg][t][r] = pr * dpd[kg][r];
           }
       }
       S::template accumulate_part_n<R>(&dv_acc[0][0], ldo, &p[0][0], S::kPartTiles, part, c, g);
@@ -263,12 +263,12 @@ struct DqPolicy {
       for (int t = 0; t < S::kPartTiles; ++t) {
         const int kb = part * S::kPartTiles + t;
         const f32x4 st = S::dot_rows(lk, kb * 16 + c, g, qf);
-        const f32x4 dp = S::dot_rows(lv, kb * 16 + c, g, dof);
+        const f32x4 dpd = S::dot_rows(lv, kb * 16 + c, g, dof, f32x4{-dd, -dd, -dd, -dd});   // dP - D
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float pr = fast_exp2(fmaf(st[r], sl2, -lse2));
           if (diag && kb * 16 + 4 * g + r > q_in_blk) pr = 0.f;
-          ds[t][r] = pr * (dp[r] - dd);
+          ds[t][r] = pr * dpd[r];
         }
       }
       S::accumulate_part(acc, lk, ds, part, c, g);

@@ -150,9 +150,11 @@ struct AttnShape {
     }
   }
 
-  // C tile: staged rows 16*tile .. +15 (this lane's row = 16*tile + c) x the fragment.
-  __device__ static __forceinline__ f32x4 dot_rows(const unsigned char *lds, int row, int g, const QFrag &qf) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // C tile: staged rows 16*tile .. +15 (this lane's row = 16*tile + c) x the fragment,
+  // added to `init` (the accumulator's starting value).
+  __device__ static __forceinline__ f32x4 dot_rows(const unsigned char *lds, int row, int g, const QFrag &qf,
+                                                   f32x4 init = f32x4{0.f, 0.f, 0.f, 0.f}) {
+    f32x4 acc = init;
     if constexpr (kBf16) {
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
@@ -173,13 +175,13 @@ struct AttnShape {
   // K-step feeds all N products.
   template <int N>
   __device__ static __forceinline__ void dot_rows_n(const unsigned char *lds, int row, int g, const QFrag *f,
-                                                    f32x4 *c) {
+                                                    f32x4 *c, f32x4 init = f32x4{0.f, 0.f, 0.f, 0.f}) {
     if constexpr (N == 1) {
-      c[0] = dot_rows(lds, row, g, f[0]);
+      c[0] = dot_rows(lds, row, g, f[0], init);
     } else {
       static_assert(kBf16, "several fragments per read: bf16 only");
 #pragma unroll
-      for (int n = 0; n < N; ++n) c[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < N; ++n) c[n] = init;
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lds + chunk_off(row, 4 * ks + g));

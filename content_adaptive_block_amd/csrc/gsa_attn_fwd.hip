@@ -34,6 +34,9 @@ namespace gsa {
 namespace {
 
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+// Score of a masked key and the initial running max: finite (the build assumes finite
+// math), and exp2 of it minus any real score is exactly 0.
+constexpr float kMaskedScore = -1.0e30f;
 
 #ifndef GSA_FWD_GROUPS
 #define GSA_FWD_GROUPS 1
@@ -74,7 +77,7 @@ struct FwdPolicy {
     for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int db = 0; db < S::kDB; ++db) acc[r][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_run[r] = -INFINITY;
+      m_run[r] = kMaskedScore;
       l_part[r] = 0.f;
     }
   }
@@ -103,11 +106,11 @@ struct FwdPolicy {
         for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
-            if (kb * 16 + 4 * g + rr > q0 + 16 * r) st[r][kb][rr] = -INFINITY;
+            if (kb * 16 + 4 * g + rr > q0 + 16 * r) st[r][kb][rr] = kMaskedScore;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float mx = -INFINITY;
+      float mx = kMaskedScore;
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
@@ -151,7 +154,10 @@ struct FwdPolicy {
 };
 
 template <typename T, int BLK, int HD>
-__global__ __launch_bounds__((BLK / (16 * fwd_groups<T, BLK, HD>()) * 64)) void attn_fwd_kernel(
+// At head_dim <= 64 the kernel is asked to fit five waves per SIMD (<= 96 VGPRs): the
+// three-tile ring lets five workgroups share a CU's LDS, and registers must not be the
+// tighter limit.
+__global__ __launch_bounds__((BLK / (16 * fwd_groups<T, BLK, HD>()) * 64), (HD <= 64 ? 5 : 1)) void attn_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
     float *__restrict__ lse, WorkLists wl, float sl2) {
   constexpr int R = fwd_groups<T, BLK, HD>();
