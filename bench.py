@@ -187,6 +187,61 @@ def cpu_baseline(wl, x_bytes, tensors, masks_np, budget_s: float):
             "seconds": secs}
 
 
+class DevicePath:
+    """Device buffers of one workload and its step: upload c, build the mask, forward,
+    and (for backward workloads) dQ then dK/dV, all on the current stream."""
+
+    def __init__(self, torch, gsa, wl, c, t, dev):
+        self.torch, self.gsa, self.wl, self.t = torch, gsa, wl, t
+        self.c_host = torch.from_numpy(c).pin_memory()
+        self.c_dev = torch.empty_like(self.c_host, device=dev)
+        self.mask = gsa.GsaMask.empty(wl.batch, wl.n_blocks, wl.window, wl.n_heads, dev)
+        self.o = torch.empty_like(t["q"])
+        self.lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device=dev)
+        self.grads = tuple(torch.empty_like(t["q"]) for _ in range(3)) if wl.backward else None
+        self.ws = torch.empty_like(self.lse)
+        self.stream = torch.cuda.current_stream(dev)
+        self.kernels = KERNELS if wl.backward else KERNELS[:2]
+
+    def events(self):
+        return [self.torch.cuda.Event(enable_timing=True) for _ in range(len(self.kernels) + 1)]
+
+    def step(self, ev=None):
+        gsa, wl, t = self.gsa, self.wl, self.t
+        if ev is not None:
+            ev[0].record(self.stream)
+        self.c_dev.copy_(self.c_host, non_blocking=True)
+        gsa.gsa_build_mask(self.c_dev, wl.window, wl.n_heads, out=self.mask)
+        if ev is not None:
+            ev[1].record(self.stream)
+        gsa.gsa_attn_fwd(t["q"], t["k"], t["v"], self.mask, wl.block, out=self.o, lse=self.lse)
+        if ev is not None:
+            ev[2].record(self.stream)
+        if wl.backward:
+            for i, stage in enumerate(("dq", "dkdv")):
+                gsa.gsa_attn_bwd(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], self.mask, wl.block,
+                                 workspace=self.ws, out=self.grads, stage=stage)
+                if ev is not None:
+                    ev[3 + i].record(self.stream)
+
+    def time(self, steps: int, warmup: int):
+        """(ms per step over `steps` back-to-back steps, mean ms per kernel)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [self.events() for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(self.stream)
+        for k in range(steps):
+            self.step(evs[k])
+        end.record(self.stream)
+        torch.cuda.synchronize()
+        per = {nm: [ev[i].elapsed_time(ev[i + 1]) for ev in evs] for i, nm in enumerate(self.kernels)}
+        return start.elapsed_time(end) / steps, {nm: float(np.mean(v)) for nm, v in per.items()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +249,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5); 4 is the headline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0: skip)")
+    ap.add_argument("--dense", action="store_true",
+                    help="time the dense causal variant of the workload (window N - 1, every head local)")
+    ap.add_argument("--dense-steps", type=int, default=5,
+                    help="also time this many steps of the dense causal variant for comparison (0: skip)")
+    ap.add_argument("--pipeline-steps", type=int, default=20,
+                    help="batches for the serial vs pipelined host-stage comparison (0: skip)")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps timed one by one after a 512 MiB cache flush (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -218,6 +279,8 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.config]
+    if args.dense:
+        wl = synth.dense_causal(wl)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     if args.copy_mib > 0:   # reads and writes copy_mib MiB per launch, 16-byte vector accesses
@@ -245,49 +308,9 @@ def main():
         gsa.gsa_prepare(x, wl.block, n_threads=1)
     prep1_ms = (time.perf_counter() - t0) / 3 * 1e3
 
-    c_host = torch.from_numpy(c).pin_memory()
-    c_dev = torch.empty_like(c_host, device=dev)
-    mask = gsa.GsaMask.empty(wl.batch, wl.n_blocks, wl.window, wl.n_heads, dev)
-    o = torch.empty_like(t["q"])
-    lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device=dev)
-    grads = tuple(torch.empty_like(t["q"]) for _ in range(3))
-    ws = torch.empty_like(lse)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record(stream)
-        mark(0)
-        c_dev.copy_(c_host, non_blocking=True)
-        gsa.gsa_build_mask(c_dev, wl.window, wl.n_heads, out=mask)
-        mark(1)
-        gsa.gsa_attn_fwd(t["q"], t["k"], t["v"], mask, wl.block, out=o, lse=lse)
-        mark(2)
-        if wl.backward:
-            for i, stage in enumerate(("dq", "dkdv")):
-                gsa.gsa_attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], mask, wl.block, workspace=ws,
-                                 out=grads, stage=stage)
-                mark(3 + i)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    n_ev = 5 if wl.backward else 3
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        step(evs[k])
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-    per = {nm: [] for nm in KERNELS[:n_ev - 1]}
-    for ev in evs:
-        for i, nm in enumerate(KERNELS[:n_ev - 1]):
-            per[nm].append(ev[i].elapsed_time(ev[i + 1]))
-    kern_ms = {nm: float(np.mean(v)) for nm, v in per.items()}
+    path = DevicePath(torch, gsa, wl, c, t, dev)
+    ms_step, kern_ms = path.time(args.steps, args.warmup)
+    mask = path.mask
 
     # Cold-cache steps: a 512 MiB write (more than the 256 MB MALL) before each step,
     # outside the events that time it.
@@ -297,15 +320,67 @@ def main():
         cold_ms = []
         for _ in range(args.cold_steps):
             flush.fill_(1.0)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-            step(ev)
+            ev = path.events()
+            path.step(ev)
             torch.cuda.synchronize()
-            cold_ms.append([ev[i].elapsed_time(ev[i + 1]) for i in range(n_ev - 1)])
+            cold_ms.append([ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)])
         del flush
         cold_arr = np.array(cold_ms)
         cold = {"steps": args.cold_steps, "ms_per_step": round(float(np.median(cold_arr.sum(axis=1))), 4),
                 "kernels_ms": {nm: round(float(np.median(cold_arr[:, i])), 4)
-                               for i, nm in enumerate(KERNELS[:n_ev - 1])}}
+                               for i, nm in enumerate(path.kernels)}}
+
+    # Host-stage pipeline: the gzip sizes of batch k + 1 are computed by the persistent
+    # pool while the device runs batch k, against the serial order (sizes, then device).
+    pipeline = None
+    if args.pipeline_steps > 0:
+        xs = [x, np.ascontiguousarray(np.roll(x, wl.block, axis=1))]   # two batches, masks differ
+        bufs = [torch.empty(c.shape, dtype=torch.int32).pin_memory() for _ in xs]
+        threads = max(1, (os.cpu_count() or 2) - 1)
+        saved = path.c_host
+        k_steps = args.pipeline_steps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(k_steps):
+            bufs[k % 2].numpy()[...] = gsa.gsa_prepare(xs[k % 2], wl.block, n_threads=threads)
+            path.c_host = bufs[k % 2]
+            path.step()
+            torch.cuda.synchronize()
+        serial = (time.perf_counter() - t0) / k_steps * 1e3
+        with gsa.PrepPool(threads) as pool:
+            pool.submit(xs[0], wl.block, bufs[0])
+            pool.wait()
+            prev = None
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(k_steps):
+                path.c_host = bufs[k % 2]
+                path.step()
+                done = torch.cuda.Event()
+                done.record(path.stream)
+                if prev is not None:
+                    prev.synchronize()   # batch k - 1 (the other buffer's copy) has finished
+                if k + 1 < k_steps:
+                    pool.submit(xs[(k + 1) % 2], wl.block, bufs[(k + 1) % 2])
+                    pool.wait()
+                prev = done
+            torch.cuda.synchronize()
+            pipelined = (time.perf_counter() - t0) / k_steps * 1e3
+        path.c_host = saved
+        pipeline = {"batches": k_steps, "host_threads": threads, "serial_ms_per_batch": round(serial, 4),
+                    "pipelined_ms_per_batch": round(pipelined, 4), "device_ms_per_step": round(ms_step, 4)}
+
+    # The same shape as dense causal attention (window >= N - 1, every head local) through
+    # the same kernels: the wall-clock the sparsity saves.
+    dense = None
+    if args.dense_steps > 0 and wl.window < wl.n_blocks - 1:
+        dwl = synth.dense_causal(wl)
+        dpath = DevicePath(torch, gsa, dwl, c, t, dev)
+        d_ms, d_kern = dpath.time(args.dense_steps, 2)
+        dense = {"workload": dwl.name, "ms_per_step": round(d_ms, 4),
+                 "kernels_ms": {nm: round(v, 4) for nm, v in d_kern.items()},
+                 "sparse_speedup": round(d_ms / ms_step, 2)}
+        del dpath
 
     n_edges = mask.n_edges.cpu().numpy().reshape(wl.batch, 3)
     n_lit = mask.n_literal.cpu().numpy()[:wl.batch]
@@ -352,7 +427,8 @@ def main():
         "token_exact_tflops": round((4 + (10 if wl.backward else 0)) * wl.head_dim * tok / (ms_step * 1e-3) / 1e12, 3),
         "kept_tiles": tiles, "literal_blocks": n_lit.tolist(),
         "host_prepare_ms": {"all_cores": round(prep_ms, 3), "one_thread": round(prep1_ms, 3)},
-        "kernels": kernels, "roofline": roof, "cold": cold,
+        "kernels": kernels, "roofline": roof, "cold": cold, "dense_causal": dense,
+        "host_pipeline": pipeline,
     }
     if args.cpu_budget > 0:
         rec["cpu_baseline"] = cpu_baseline(wl, x, host_t, None, args.cpu_budget)

@@ -21,7 +21,8 @@ import numpy as np
 import torch  # loaded first: libgsa binds to the HIP runtime torch has already mapped
 
 __all__ = [
-    "GsaError", "GsaMask", "lib_path", "load_library", "gsa_prepare", "gsa_mask_sizes", "gsa_build_mask",
+    "GsaError", "GsaMask", "PrepPool", "lib_path", "load_library", "gsa_prepare", "gsa_mask_sizes",
+    "gsa_build_mask",
     "gsa_attn_fwd", "gsa_attn_bwd", "attention", "zlib_version", "default_head_counts",
     "GSA_OK", "GSA_ERR_ARG", "GSA_ERR_SHAPE", "GSA_ERR_ZLIB", "GSA_ERR_HIP", "GSA_ERR_UNSUPPORTED",
 ]
@@ -84,6 +85,12 @@ def load_library():
     lib.gsa_abi_version.argtypes, lib.gsa_abi_version.restype = [], i32
     lib.gsa_prepare.argtypes = [vp, i64, i64, i32, i32, vp]
     lib.gsa_prepare.restype = i32
+    lib.gsa_prep_pool_create.argtypes = [i32, ctypes.POINTER(vp)]
+    lib.gsa_prep_pool_submit.argtypes = [vp, vp, i64, i64, i32, vp]
+    lib.gsa_prep_pool_wait.argtypes = [vp]
+    lib.gsa_prep_pool_destroy.argtypes = [vp]
+    for nm in ("gsa_prep_pool_create", "gsa_prep_pool_submit", "gsa_prep_pool_wait", "gsa_prep_pool_destroy"):
+        getattr(lib, nm).restype = i32
     lib.gsa_mask_sizes.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
     lib.gsa_mask_sizes.restype = i32
     lib.gsa_build_mask.argtypes = [vp, ctypes.POINTER(_Mask), vp]
@@ -143,6 +150,63 @@ def gsa_prepare(data, block: int, n_threads: int = 0) -> np.ndarray:
     st = load_library().gsa_prepare(arr.ctypes.data, batch, seq_len, block, n_threads, out.ctypes.data)
     _check(st, "gsa_prepare")
     return out
+
+
+class PrepPool:
+    """Persistent host pool for the gzip stage (gsa_prep_pool_*): ``submit`` starts a
+    batch and returns at once, ``wait`` blocks until its sizes are in ``out``."""
+
+    def __init__(self, n_threads: int = 0):
+        handle = ctypes.c_void_p()
+        _check(load_library().gsa_prep_pool_create(n_threads, ctypes.byref(handle)), "gsa_prep_pool_create")
+        self._h = handle
+        self._keep = None   # the running batch's buffers stay referenced until it is done
+
+    def submit(self, data: np.ndarray, block: int, out) -> None:
+        """Start sizes of host bytes ``data`` uint8 [B, T] into ``out`` int32 [B, T/block]
+        (a numpy array or a CPU tensor, e.g. pinned for a later device copy)."""
+        arr = np.ascontiguousarray(np.asarray(data, dtype=np.uint8))
+        if arr.ndim != 2:
+            raise ValueError("data must be [batch, seq_len]")
+        batch, seq_len = arr.shape
+        n = seq_len // block if block > 0 else 0
+        if isinstance(out, torch.Tensor):
+            if out.device.type != "cpu" or out.dtype != torch.int32 or not out.is_contiguous():
+                raise ValueError("out must be a contiguous int32 host tensor")
+            ptr, size = out.data_ptr(), out.numel()
+        else:
+            if out.dtype != np.int32 or not out.flags.c_contiguous:
+                raise ValueError("out must be a contiguous int32 array")
+            ptr, size = out.ctypes.data, out.size
+        if size != batch * n:
+            raise ValueError(f"out has {size} entries, expected {batch * n}")
+        _check(load_library().gsa_prep_pool_submit(self._h, arr.ctypes.data, batch, seq_len, block, ptr),
+               "gsa_prep_pool_submit")
+        self._keep = (arr, out)
+
+    def wait(self) -> None:
+        try:
+            _check(load_library().gsa_prep_pool_wait(self._h), "gsa_prep_pool_wait")
+        finally:
+            self._keep = None
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            load_library().gsa_prep_pool_destroy(self._h)
+        self._h = None
+        self._keep = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
 
 
 # ---------------------------------------------------------------------------------- (2)

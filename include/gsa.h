@@ -89,6 +89,33 @@ gsa_status gsa_prepare(const uint8_t *bytes, int64_t batch, int64_t seq_len, int
                        int32_t n_threads, int32_t *c_out);
 
 /* ------------------------------------------------------------------------------------
+ * (1b) Host-stage pipeline: the same sizes as gsa_prepare from a persistent pool of
+ *      deflate workers, computed asynchronously so that the next batch's sizes can be
+ *      prepared while the device runs the current batch ([note] flowchart: the gzip
+ *      stage comes before everything else on the path).
+ *
+ *   gsa_prep_pool_create   starts n_threads workers (<= 0: every online core); *pool
+ *                          receives the handle (NULL on failure).
+ *   gsa_prep_pool_submit   waits until the previous batch is done, then starts this one
+ *                          and returns at once.  Arguments as for gsa_prepare; `bytes` and
+ *                          `c_out` must stay valid until the batch is done.  If the
+ *                          previous batch failed, returns its error and starts nothing.
+ *   gsa_prep_pool_wait     blocks until the current batch is done; returns its status
+ *                          (GSA_OK if nothing was submitted).
+ *   gsa_prep_pool_destroy  waits for the current batch, stops the workers and frees the
+ *                          pool (NULL is a no-op).
+ * c_out equals gsa_prepare's output byte for byte.  One pool serves one caller thread at
+ * a time.  Errors: as gsa_prepare (synchronous ones from submit, zlib failures from the
+ * next wait or submit); NULL pool -> GSA_ERR_ARG.
+ * ------------------------------------------------------------------------------------ */
+typedef struct gsa_prep_pool gsa_prep_pool;
+gsa_status gsa_prep_pool_create(int32_t n_threads, gsa_prep_pool **pool);
+gsa_status gsa_prep_pool_submit(gsa_prep_pool *pool, const uint8_t *bytes, int64_t batch, int64_t seq_len,
+                                int32_t block, int32_t *c_out);
+gsa_status gsa_prep_pool_wait(gsa_prep_pool *pool);
+gsa_status gsa_prep_pool_destroy(gsa_prep_pool *pool);
+
+/* ------------------------------------------------------------------------------------
  * (2) Mask: literal flags and per-class block lists.
  *     [note] 核心公式 first display (l_i = 1[r_i > mean r], evaluated exactly as the
  *     integer test N * c_i > sum_j c_j of the sample), second display (the mask

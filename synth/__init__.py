@@ -20,7 +20,7 @@ tensors are those draws rounded to nearest-even by torch.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -215,3 +215,9 @@ def gen_tensors(wl: Workload, names=("q", "k", "v"), batch=None, heads=None, seq
         x = torch.from_numpy(gen_normal(wl.seed_id, streams[nm], shape, std))
         out[nm] = x if dt == torch.float32 else x.to(dt)
     return out
+
+
+def dense_causal(wl: Workload) -> Workload:
+    """The same shape as ``wl`` with every head local and a window covering the whole
+    sequence: the mask is then the full causal triangle (dense causal attention)."""
+    return replace(wl, name=wl.name + "-dense", window=wl.n_blocks - 1, n_heads=(wl.heads, 0, 0))

@@ -168,3 +168,58 @@ def test_attn_bwd_validation(lib):
 def test_status_strings(lib):
     assert lib.gsa_status_str(gsa.GSA_ERR_SHAPE) == b"GSA_ERR_SHAPE"
     assert lib.gsa_status_str(99) == b"GSA_ERR_UNKNOWN"
+
+
+# ------------------------------------------------------------------ host-stage pool
+def test_prep_pool_matches_prepare_and_oracle():
+    """Every config through one pool (block sizes change between batches), twice, with
+    results equal to gsa_prepare and to the oracle's independent zlib path."""
+    with gsa.PrepPool(3) as pool:
+        for rep in range(2):
+            for cid in (1, 2, 5, 3):
+                wl = synth.WORKLOADS[cid]
+                x = synth.gen_bytes(wl, batch=min(wl.batch, 2))
+                out = np.full((x.shape[0], x.shape[1] // wl.block), -1, dtype=np.int32)
+                pool.submit(x, wl.block, out)
+                pool.wait()
+                assert np.array_equal(out, gsa.gsa_prepare(x, wl.block)), (rep, cid)
+                if rep == 0:
+                    assert np.array_equal(out, oracle.compressed_lengths(x, wl.block)), cid
+
+
+def test_prep_pool_overlapping_submits():
+    """A submit waits for the previous batch; each output buffer gets its own batch."""
+    wl = synth.WORKLOADS[2]
+    xs = [synth.gen_bytes(wl, batch=3), np.roll(synth.gen_bytes(wl, batch=3), 17)]
+    outs = [np.zeros((3, wl.n_blocks), np.int32) for _ in xs]
+    with gsa.PrepPool(0) as pool:
+        for x, o in zip(xs, outs):
+            pool.submit(x, wl.block, o)   # the second submit waits for the first batch
+        pool.wait()
+    for x, o in zip(xs, outs):
+        assert np.array_equal(o, gsa.gsa_prepare(x, wl.block))
+
+
+def test_prep_pool_errors(lib):
+    h = ctypes.c_void_p()
+    assert lib.gsa_prep_pool_create(2, ctypes.byref(h)) == gsa.GSA_OK and h.value
+    buf = np.zeros((2, 64), np.uint8)
+    out = np.zeros((2, 4), np.int32)
+    sub = lib.gsa_prep_pool_submit
+    assert sub(h, buf.ctypes.data, -1, 64, 16, out.ctypes.data) == gsa.GSA_ERR_ARG
+    assert sub(h, buf.ctypes.data, 2, 64, 0, out.ctypes.data) == gsa.GSA_ERR_ARG
+    assert sub(h, buf.ctypes.data, 2, 60, 16, out.ctypes.data) == gsa.GSA_ERR_SHAPE
+    assert sub(h, None, 2, 64, 16, out.ctypes.data) == gsa.GSA_ERR_ARG
+    assert sub(h, buf.ctypes.data, 0, 64, 16, None) == gsa.GSA_OK          # empty batch
+    assert sub(h, buf.ctypes.data, 2, 64, 16, out.ctypes.data) == gsa.GSA_OK
+    assert lib.gsa_prep_pool_wait(h) == gsa.GSA_OK
+    assert (out > 0).all()
+    assert lib.gsa_prep_pool_wait(h) == gsa.GSA_OK                          # nothing pending
+    assert lib.gsa_prep_pool_submit(None, buf.ctypes.data, 2, 64, 16, out.ctypes.data) == gsa.GSA_ERR_ARG
+    assert lib.gsa_prep_pool_wait(None) == gsa.GSA_ERR_ARG
+    assert lib.gsa_prep_pool_destroy(h) == gsa.GSA_OK
+    assert lib.gsa_prep_pool_destroy(None) == gsa.GSA_OK
+    assert lib.gsa_prep_pool_create(1, None) == gsa.GSA_ERR_ARG
+    with gsa.PrepPool(1) as pool:
+        with pytest.raises(ValueError):
+            pool.submit(buf, 16, np.zeros((2, 3), np.int32))

@@ -237,3 +237,47 @@ def test_backward_stage_entry_points(inst):
     tol, _ = _tol(dtype)
     assert_close("dK after prep", f64(g2[1]), ref_dk, tol)
     assert_close("dV after prep", f64(g2[2]), ref_dv, tol)
+
+
+DENSE = [
+    # (instance, batch, N, heads): window N - 1 and every head local = dense causal
+    (("bf16", 64, 64), 1, 128, 2),
+    (("bf16", 128, 128), 1, 64, 2),
+    (("f32", 16, 32), 2, 64, 2),
+]
+
+
+@pytest.mark.parametrize("inst,batch,n,heads", DENSE)
+def test_dense_causal_sampled(inst, batch, n, heads):
+    """Window >= N - 1 turns every local head into plain causal attention over up to N
+    kept blocks per list (lists longer than 64 entries included)."""
+    dtype, block, hd = inst
+    n_heads, window = (heads, 0, 0), n - 1
+    log(f"  dense causal {dtype} b={block} d={hd} B={batch} N={n} H={heads}")
+    x, t = _inputs(inst, batch, n, heads)
+    res = run_path(x, block, window, n_heads, t, backward=True)
+    masks = check_mask(res["mask"], res["c"], block, window, n_heads)
+    assert np.array_equal(masks[:, 0], np.broadcast_to(np.tril(np.ones((n, n), bool)), (batch, n, n)))
+    tol, ltol = _tol(dtype)
+    rng = np.random.default_rng(n)
+    errs = {}
+    for s in range(batch):
+        for h in range(heads):
+            q, k, v, do = (f64(t[nm][s, h]) for nm in ("q", "k", "v", "do"))
+            bm = masks[s, 0]
+            for i in sorted({0, n - 1, int(rng.integers(n))}):
+                rows = np.arange(i * block, (i + 1) * block)
+                ro, rl = oracle.attn_fwd_rows(q, k, v, bm, block, rows)
+                errs.setdefault("O", []).append((f64(res["o"][s, h, rows]), ro))
+                errs.setdefault("LSE", []).append((f64(res["lse"][s, h, rows]), rl))
+                rq = oracle.attn_bwd_qblock(q, k, v, do, bm, block, i)
+                errs.setdefault("dQ", []).append((f64(res["dq"][s, h, rows]), rq))
+            for j in sorted({n - 1, n - 2, n - 1 - int(rng.integers(4))}):
+                rows = np.arange(j * block, (j + 1) * block)
+                rk, rv = oracle.attn_bwd_kblock(q, k, v, do, bm, block, j)
+                errs.setdefault("dK", []).append((f64(res["dk"][s, h, rows]), rk))
+                errs.setdefault("dV", []).append((f64(res["dv"][s, h, rows]), rv))
+    for nm, pairs in errs.items():
+        got = np.concatenate([p[0].ravel() for p in pairs])
+        ref = np.concatenate([p[1].ravel() for p in pairs])
+        assert_close(f"{nm} ({len(pairs)} sampled blocks)", got, ref, ltol if nm == "LSE" else tol)
