@@ -253,6 +253,8 @@ def main():
                     help="time the dense causal variant of the workload (window N - 1, every head local)")
     ap.add_argument("--dense-steps", type=int, default=5,
                     help="also time this many steps of the dense causal variant for comparison (0: skip)")
+    ap.add_argument("--layer-steps", type=int, default=5,
+                    help="fwd+bwd steps of the ByteLM attention layer (projections + kernels) (0: skip)")
     ap.add_argument("--pipeline-steps", type=int, default=20,
                     help="batches for the serial vs pipelined host-stage comparison (0: skip)")
     ap.add_argument("--cold-steps", type=int, default=10,
@@ -370,6 +372,35 @@ def main():
         pipeline = {"batches": k_steps, "host_threads": threads, "serial_ms_per_batch": round(serial, 4),
                     "pipelined_ms_per_batch": round(pipelined, 4), "device_ms_per_step": round(ms_step, 4)}
 
+    # ByteLM attention layer at this shape: Q/K/V and output projections (D = H d) around
+    # the same kernels, forward and backward.
+    layer = None
+    if args.layer_steps > 0 and wl.backward and wl.dtype == "bf16":
+        from content_adaptive_block_amd.layer import GsaAttentionLayer
+        dm = wl.heads * wl.head_dim
+        torch.manual_seed(0)
+        lyr = GsaAttentionLayer(dm, wl.heads, wl.head_dim, wl.block, wl.n_heads, device=dev)
+        xin = (torch.randn(wl.batch, wl.seq_len, dm, device=dev) * 0.5).to(torch.bfloat16).requires_grad_(True)
+        gy = torch.randn(wl.batch, wl.seq_len, dm, device=dev).to(torch.bfloat16)
+
+        def layer_step():
+            lyr(xin, path.mask).backward(gy)
+
+        for _ in range(2):
+            layer_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(path.stream)
+        for _ in range(args.layer_steps):
+            layer_step()
+        e1.record(path.stream)
+        torch.cuda.synchronize()
+        l_ms = e0.elapsed_time(e1) / args.layer_steps
+        attn_ms = kern_ms["fwd"] + kern_ms.get("bwd_dq", 0.0) + kern_ms.get("bwd_dkdv", 0.0)
+        layer = {"d_model": dm, "ms_fwd_bwd": round(l_ms, 4), "attention_ms": round(attn_ms, 4),
+                 "attention_share": round(attn_ms / l_ms, 3)}
+        del lyr, xin, gy
+
     # The same shape as dense causal attention (window >= N - 1, every head local) through
     # the same kernels: the wall-clock the sparsity saves.
     dense = None
@@ -428,7 +459,7 @@ def main():
         "kept_tiles": tiles, "literal_blocks": n_lit.tolist(),
         "host_prepare_ms": {"all_cores": round(prep_ms, 3), "one_thread": round(prep1_ms, 3)},
         "kernels": kernels, "roofline": roof, "cold": cold, "dense_causal": dense,
-        "host_pipeline": pipeline,
+        "host_pipeline": pipeline, "layer": layer,
     }
     if args.cpu_budget > 0:
         rec["cpu_baseline"] = cpu_baseline(wl, x, host_t, None, args.cpu_budget)
