@@ -191,8 +191,9 @@ class DevicePath:
     """Device buffers of one workload and its step: upload c, build the mask, forward,
     and (for backward workloads) dQ then dK/dV, all on the current stream."""
 
-    def __init__(self, torch, gsa, wl, c, t, dev):
+    def __init__(self, torch, gsa, wl, c, t, dev, blocks=None):
         self.torch, self.gsa, self.wl, self.t = torch, gsa, wl, t
+        self.blocks = blocks   # a given block mask (uint8 [B, 3, N, N]) instead of the gzip one
         self.c_host = torch.from_numpy(c).pin_memory()
         self.c_dev = torch.empty_like(self.c_host, device=dev)
         self.mask = gsa.GsaMask.empty(wl.batch, wl.n_blocks, wl.window, wl.n_heads, dev)
@@ -210,8 +211,11 @@ class DevicePath:
         gsa, wl, t = self.gsa, self.wl, self.t
         if ev is not None:
             ev[0].record(self.stream)
-        self.c_dev.copy_(self.c_host, non_blocking=True)
-        gsa.gsa_build_mask(self.c_dev, wl.window, wl.n_heads, out=self.mask)
+        if self.blocks is None:
+            self.c_dev.copy_(self.c_host, non_blocking=True)
+            gsa.gsa_build_mask(self.c_dev, wl.window, wl.n_heads, out=self.mask)
+        else:
+            gsa.gsa_build_mask_from_blocks(self.blocks, wl.n_heads, out=self.mask)
         if ev is not None:
             ev[1].record(self.stream)
         gsa.gsa_attn_fwd(t["q"], t["k"], t["v"], self.mask, wl.block, out=self.o, lse=self.lse)
@@ -253,6 +257,8 @@ def main():
                     help="time the dense causal variant of the workload (window N - 1, every head local)")
     ap.add_argument("--dense-steps", type=int, default=5,
                     help="also time this many steps of the dense causal variant for comparison (0: skip)")
+    ap.add_argument("--bigbird-steps", type=int, default=10,
+                    help="steps of a BigBird-style fixed mask at the same shape, for comparison (0: skip)")
     ap.add_argument("--layer-steps", type=int, default=5,
                     help="fwd+bwd steps of the ByteLM attention layer (projections + kernels) (0: skip)")
     ap.add_argument("--pipeline-steps", type=int, default=20,
@@ -401,6 +407,25 @@ def main():
                  "attention_share": round(attn_ms / l_ms, 3)}
         del lyr, xin, gy
 
+    # BigBird-style fixed mask (window w, one global block, one random block per row; the
+    # pages give no BigBird parameters) at this shape through the same kernels.
+    bigbird = None
+    if args.bigbird_steps > 0:
+        import dataclasses
+        n_global, n_random = 1, 1
+        picks = synth.bigbird_picks(wl, n_random)
+        blocks = gsa.gsa_bigbird_blocks(torch.from_numpy(picks).to(dev), wl.window, n_global)
+        bwl = dataclasses.replace(wl, name=wl.name + "-bigbird", n_heads=(wl.heads, 0, 0))
+        bpath = DevicePath(torch, gsa, bwl, c, t, dev, blocks=blocks)
+        b_ms, b_kern = bpath.time(args.bigbird_steps, 2)
+        b_edges = bpath.mask.n_edges.cpu().numpy().reshape(wl.batch, 3)
+        b_tiles = kept_tiles(b_edges, bwl.n_heads)
+        b_flops = (4 + (10 if wl.backward else 0)) * wl.block * wl.block * wl.head_dim * b_tiles
+        bigbird = {"window": wl.window, "n_global": n_global, "n_random": n_random, "kept_tiles": b_tiles,
+                   "ms_per_step": round(b_ms, 4), "kernels_ms": {nm: round(v, 4) for nm, v in b_kern.items()},
+                   "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 3)}
+        del bpath, blocks
+
     # The same shape as dense causal attention (window >= N - 1, every head local) through
     # the same kernels: the wall-clock the sparsity saves.
     dense = None
@@ -459,7 +484,7 @@ def main():
         "kept_tiles": tiles, "literal_blocks": n_lit.tolist(),
         "host_prepare_ms": {"all_cores": round(prep_ms, 3), "one_thread": round(prep1_ms, 3)},
         "kernels": kernels, "roofline": roof, "cold": cold, "dense_causal": dense,
-        "host_pipeline": pipeline, "layer": layer,
+        "host_pipeline": pipeline, "layer": layer, "bigbird": bigbird,
     }
     if args.cpu_budget > 0:
         rec["cpu_baseline"] = cpu_baseline(wl, x, host_t, None, args.cpu_budget)

@@ -22,7 +22,7 @@ import torch  # loaded first: libgsa binds to the HIP runtime torch has already 
 
 __all__ = [
     "GsaError", "GsaMask", "PrepPool", "lib_path", "load_library", "gsa_prepare", "gsa_mask_sizes",
-    "gsa_build_mask",
+    "gsa_build_mask", "gsa_build_mask_from_blocks", "gsa_bigbird_blocks",
     "gsa_attn_fwd", "gsa_attn_bwd", "attention", "zlib_version", "default_head_counts",
     "GSA_OK", "GSA_ERR_ARG", "GSA_ERR_SHAPE", "GSA_ERR_ZLIB", "GSA_ERR_HIP", "GSA_ERR_UNSUPPORTED",
 ]
@@ -95,6 +95,10 @@ def load_library():
     lib.gsa_mask_sizes.restype = i32
     lib.gsa_build_mask.argtypes = [vp, ctypes.POINTER(_Mask), vp]
     lib.gsa_build_mask.restype = i32
+    lib.gsa_build_mask_from_blocks.argtypes = [vp, ctypes.POINTER(_Mask), vp]
+    lib.gsa_build_mask_from_blocks.restype = i32
+    lib.gsa_bigbird_blocks.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp]
+    lib.gsa_bigbird_blocks.restype = i32
     lib.gsa_attn_fwd.argtypes = [ctypes.POINTER(_FwdArgs), ctypes.POINTER(_Mask), vp]
     lib.gsa_attn_fwd.restype = i32
     for nm in ("gsa_attn_bwd", "gsa_attn_bwd_prep", "gsa_attn_bwd_dkdv", "gsa_attn_bwd_dq"):
@@ -278,6 +282,40 @@ def gsa_build_mask(c, window: int, n_heads, device=None, out: GsaMask | None = N
     _check(load_library().gsa_build_mask(c.data_ptr(), ctypes.byref(ms), _stream_ptr(device)),
            "gsa_build_mask")
     return m
+
+
+def gsa_build_mask_from_blocks(blocks: torch.Tensor, n_heads, out: GsaMask | None = None) -> GsaMask:
+    """Block lists and work order of a given block mask ``blocks`` (device uint8
+    [B, 3, N, N]; entries above the diagonal ignored, the diagonal always kept)."""
+    if not (isinstance(blocks, torch.Tensor) and blocks.is_cuda and blocks.dtype == torch.uint8
+            and blocks.dim() == 4 and blocks.shape[1] == 3 and blocks.shape[2] == blocks.shape[3]):
+        raise ValueError("blocks must be a device uint8 tensor [B, 3, N, N]")
+    blocks = blocks.contiguous()
+    batch, n = blocks.shape[0], blocks.shape[2]
+    m = out if out is not None else GsaMask.empty(batch, n, 0, n_heads, blocks.device)
+    if (m.batch, m.n_blocks) != (batch, n):
+        raise ValueError("preallocated mask has another shape")
+    m.window = 0
+    ms = m.struct()
+    _check(load_library().gsa_build_mask_from_blocks(blocks.data_ptr(), ctypes.byref(ms), _stream_ptr(blocks.device)),
+           "gsa_build_mask_from_blocks")
+    return m
+
+
+def gsa_bigbird_blocks(random: torch.Tensor, window: int, n_global: int, out: torch.Tensor | None = None):
+    """BigBird-style causal block mask (class 0; classes 1, 2 diagonal only) as device
+    uint8 [B, 3, N, N], from the random picks ``random`` device int32 [B, N, r] (each
+    entry of row i in 0..i)."""
+    if not (isinstance(random, torch.Tensor) and random.is_cuda and random.dtype == torch.int32
+            and random.dim() == 3):
+        raise ValueError("random must be a device int32 tensor [B, N, r]")
+    random = random.contiguous()
+    batch, n, r = random.shape
+    if out is None:
+        out = torch.empty((batch, 3, n, n), dtype=torch.uint8, device=random.device)
+    _check(load_library().gsa_bigbird_blocks(batch, n, window, n_global, r, random.data_ptr(), out.data_ptr(),
+                                             _stream_ptr(random.device)), "gsa_bigbird_blocks")
+    return out
 
 
 # ---------------------------------------------------------------------------------- (3), (4)

@@ -137,6 +137,29 @@ gsa_status gsa_build_mask(const int32_t *c_dev, const gsa_mask *m, hipStream_t s
   return launch_build_mask(c_dev, *m, stream);
 }
 
+gsa_status gsa_build_mask_from_blocks(const uint8_t *blocks_dev, const gsa_mask *m, hipStream_t stream) {
+  clear_error();
+  gsa_status st = check_mask(m, true);
+  if (st != GSA_OK) return st;
+  if (m->batch == 0) return GSA_OK;
+  if (!blocks_dev) return fail(GSA_ERR_ARG, "blocks_dev is NULL");
+  return launch_mask_from_blocks(blocks_dev, *m, stream);
+}
+
+gsa_status gsa_bigbird_blocks(int64_t batch, int32_t n_blocks, int32_t window, int32_t n_global,
+                              int32_t n_random, const int32_t *random_dev, uint8_t *blocks_dev,
+                              hipStream_t stream) {
+  clear_error();
+  if (batch < 0) return fail(GSA_ERR_ARG, "batch %lld < 0", (long long)batch);
+  if (window < 0 || n_global < 0 || n_random < 0)
+    return fail(GSA_ERR_ARG, "window, n_global and n_random must be >= 0");
+  if (batch == 0) return GSA_OK;
+  if (n_blocks < 1 || n_blocks > GSA_MAX_BLOCKS)
+    return fail(GSA_ERR_UNSUPPORTED, "n_blocks %d outside 1..%d", n_blocks, GSA_MAX_BLOCKS);
+  if (!blocks_dev || (n_random > 0 && !random_dev)) return fail(GSA_ERR_ARG, "blocks_dev or random_dev is NULL");
+  return launch_bigbird(batch, n_blocks, window, n_global, n_random, random_dev, blocks_dev, stream);
+}
+
 gsa_status gsa_attn_fwd(const gsa_fwd_args *a, const gsa_mask *m, hipStream_t stream) {
   clear_error();
   gsa_status st = check_fwd(a, m);

@@ -60,77 +60,18 @@ __device__ __forceinline__ int find_segment(const int *start, int n, int e) {
   return lo;
 }
 
-__global__ __launch_bounds__(kMaskThreads) void mask_kernel(
-    const int32_t *__restrict__ c, int n, int w, uint8_t *__restrict__ flags,
-    int32_t *__restrict__ n_literal, int32_t *__restrict__ row_ptr, int32_t *__restrict__ col_idx,
-    int32_t *__restrict__ col_ptr, int32_t *__restrict__ row_idx, int64_t *__restrict__ n_edges,
-    int64_t cap, int32_t *__restrict__ sched, int64_t batch) {
-  __shared__ int s_prefix[GSA_MAX_BLOCKS + 1];   // # literal blocks before position i
-  __shared__ int s_list[GSA_MAX_BLOCKS];         // literal block ids, ascending
-  __shared__ int s_start[6][GSA_MAX_BLOCKS + 1]; // row starts (k), then column starts (3 + k)
-  __shared__ long long s_sum[kMaskWaves];
-  __shared__ int s_wave[6][kMaskWaves];
-  __shared__ int s_cnt[6][kMaskWaves][kOrderKeys];
-
+// From the six list lengths of this thread's block t (rows of classes 0..2, then columns):
+// one exclusive scan into row_ptr / col_ptr (also kept in s_start), the edge counts, and
+// the work-order data (key histograms and packed ranks) in sched.  Every thread of the
+// workgroup calls it (it synchronises); s_cnt must be zero and visible on entry.
+__device__ void lengths_to_lists(const int (&len)[6], int n, int64_t s, int64_t batch, int32_t *__restrict__ row_ptr,
+                                 int32_t *__restrict__ col_ptr, int64_t *__restrict__ n_edges,
+                                 int32_t *__restrict__ sched, int (*s_start)[GSA_MAX_BLOCKS + 1],
+                                 int (*s_wave)[kMaskWaves], int (*s_cnt)[kMaskWaves][kOrderKeys]) {
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-  const int64_t s = blockIdx.x;
   const bool valid = t < n;
-  // Waves holding blocks; the others only help with the list entries.
   const int active = (n + kWave - 1) / kWave;
   const bool busy = wave < active;
-  const int ci = valid ? c[s * n + t] : 0;
-  for (int x = t; x < 6 * kMaskWaves * kOrderKeys; x += kMaskThreads) (&s_cnt[0][0][0])[x] = 0;
-
-  // Sum of c over the sample, exactly, in 64 bits.
-  if (busy) {
-    long long part = ci;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
-    if (lane == 0) s_sum[wave] = part;
-  }
-  __syncthreads();
-  long long sum = 0;
-  for (int w2 = 0; w2 < active; ++w2) sum += s_sum[w2];
-
-  // l_i = [N c_i > sum c]  <=>  r_i > mean r.
-  const bool lit = valid && (long long)n * ci > sum;
-  const uint64_t bal = __ballot(lit);
-  const int below = __popcll(bal & lanes_below(lane));
-  if (lane == 0) s_wave[0][wave] = __popcll(bal);
-  __syncthreads();
-  int wave_base = 0, n_lit = 0;
-  for (int w2 = 0; w2 < active; ++w2) {
-    if (w2 < wave) wave_base += s_wave[0][w2];
-    n_lit += s_wave[0][w2];
-  }
-  const int rank = wave_base + below;   // literal blocks j < t
-  if (valid) {
-    flags[s * n + t] = lit ? 1 : 0;
-    s_prefix[t] = rank;
-    if (lit) s_list[rank] = t;
-  }
-  if (t == 0) {
-    s_prefix[n] = n_lit;
-    n_literal[s] = n_lit;
-  }
-  __syncthreads();
-
-  // List lengths in closed form (w >= n - 1 behaves like w = n): rows k, columns 3 + k.
-  const int ww = w < n ? w : n;
-  int len[6] = {0, 0, 0, 0, 0, 0};
-  if (valid) {
-    const int win = (t < ww ? t : ww) + 1;
-    len[0] = win;
-    len[1] = lit ? rank + 1 : 1;
-    len[2] = win + (lit ? s_prefix[t - ww > 0 ? t - ww : 0] : 0);
-    const int after = n - 1 - t;
-    const int cwin = (after < ww ? after : ww) + 1;
-    const int beyond = t + ww + 1 < n ? t + ww + 1 : n;
-    len[3] = cwin;
-    len[4] = lit ? n_lit - rank : 1;
-    len[5] = cwin + (lit ? n_lit - s_prefix[beyond] : 0);
-  }
-
   // One exclusive scan of the six lengths, and the ranks among equal keys: lanes with the
   // same key agree on every key bit, so AND-ing the ballots of the bits (or of their
   // complements) gives the wave's lanes with this lane's key.
@@ -208,6 +149,81 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
           ((s_cnt[q][wave][key[q]] + in_rank[q]) << 4) | key[q];
   }
 
+}
+
+__global__ __launch_bounds__(kMaskThreads) void mask_kernel(
+    const int32_t *__restrict__ c, int n, int w, uint8_t *__restrict__ flags,
+    int32_t *__restrict__ n_literal, int32_t *__restrict__ row_ptr, int32_t *__restrict__ col_idx,
+    int32_t *__restrict__ col_ptr, int32_t *__restrict__ row_idx, int64_t *__restrict__ n_edges,
+    int64_t cap, int32_t *__restrict__ sched, int64_t batch) {
+  __shared__ int s_prefix[GSA_MAX_BLOCKS + 1];   // # literal blocks before position i
+  __shared__ int s_list[GSA_MAX_BLOCKS];         // literal block ids, ascending
+  __shared__ int s_start[6][GSA_MAX_BLOCKS + 1]; // row starts (k), then column starts (3 + k)
+  __shared__ long long s_sum[kMaskWaves];
+  __shared__ int s_wave[6][kMaskWaves];
+  __shared__ int s_cnt[6][kMaskWaves][kOrderKeys];
+
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int64_t s = blockIdx.x;
+  const bool valid = t < n;
+  // Waves holding blocks; the others only help with the list entries.
+  const int active = (n + kWave - 1) / kWave;
+  const bool busy = wave < active;
+  const int ci = valid ? c[s * n + t] : 0;
+  for (int x = t; x < 6 * kMaskWaves * kOrderKeys; x += kMaskThreads) (&s_cnt[0][0][0])[x] = 0;
+
+  // Sum of c over the sample, exactly, in 64 bits.
+  if (busy) {
+    long long part = ci;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+    if (lane == 0) s_sum[wave] = part;
+  }
+  __syncthreads();
+  long long sum = 0;
+  for (int w2 = 0; w2 < active; ++w2) sum += s_sum[w2];
+
+  // l_i = [N c_i > sum c]  <=>  r_i > mean r.
+  const bool lit = valid && (long long)n * ci > sum;
+  const uint64_t bal = __ballot(lit);
+  const int below = __popcll(bal & lanes_below(lane));
+  if (lane == 0) s_wave[0][wave] = __popcll(bal);
+  __syncthreads();
+  int wave_base = 0, n_lit = 0;
+  for (int w2 = 0; w2 < active; ++w2) {
+    if (w2 < wave) wave_base += s_wave[0][w2];
+    n_lit += s_wave[0][w2];
+  }
+  const int rank = wave_base + below;   // literal blocks j < t
+  if (valid) {
+    flags[s * n + t] = lit ? 1 : 0;
+    s_prefix[t] = rank;
+    if (lit) s_list[rank] = t;
+  }
+  if (t == 0) {
+    s_prefix[n] = n_lit;
+    n_literal[s] = n_lit;
+  }
+  __syncthreads();
+
+  // List lengths in closed form (w >= n - 1 behaves like w = n): rows k, columns 3 + k.
+  const int ww = w < n ? w : n;
+  int len[6] = {0, 0, 0, 0, 0, 0};
+  if (valid) {
+    const int win = (t < ww ? t : ww) + 1;
+    len[0] = win;
+    len[1] = lit ? rank + 1 : 1;
+    len[2] = win + (lit ? s_prefix[t - ww > 0 ? t - ww : 0] : 0);
+    const int after = n - 1 - t;
+    const int cwin = (after < ww ? after : ww) + 1;
+    const int beyond = t + ww + 1 < n ? t + ww + 1 : n;
+    len[3] = cwin;
+    len[4] = lit ? n_lit - rank : 1;
+    len[5] = cwin + (lit ? n_lit - s_prefix[beyond] : 0);
+  }
+
+  lengths_to_lists(len, n, s, batch, row_ptr, col_ptr, n_edges, sched, s_start, s_wave, s_cnt);
+
   // List entries, one thread each.  Row i of class k, entry e of it:
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
@@ -253,6 +269,82 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
       out[e0] = i;
     }
   }
+}
+
+
+// ---------------------------------------------------------------------------------------
+// Lists of a caller-given block mask: u8 [B, 3, N, N], entry (s, k, i, j) nonzero when
+// query block i of class k keeps kv-block j.  The lists follow the causal reading of the
+// gzip mask: entries above the diagonal are ignored and the diagonal is always kept, so
+// the attention kernels see the same list shape as for the gzip mask.  One workgroup per
+// sample, thread t owns row t and column t of every class; flags and L are set to zero.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ bool block_kept(const uint8_t *m, int n, int i, int j) {
+  return j == i || (j < i && m[(int64_t)i * n + j] != 0);
+}
+
+__global__ __launch_bounds__(kMaskThreads) void blocks_kernel(
+    const uint8_t *__restrict__ blocks, int n, uint8_t *__restrict__ flags, int32_t *__restrict__ n_literal,
+    int32_t *__restrict__ row_ptr, int32_t *__restrict__ col_idx, int32_t *__restrict__ col_ptr,
+    int32_t *__restrict__ row_idx, int64_t *__restrict__ n_edges, int64_t cap, int32_t *__restrict__ sched,
+    int64_t batch) {
+  __shared__ int s_start[6][GSA_MAX_BLOCKS + 1];
+  __shared__ int s_wave[6][kMaskWaves];
+  __shared__ int s_cnt[6][kMaskWaves][kOrderKeys];
+  const int t = threadIdx.x;
+  const int64_t s = blockIdx.x;
+  const bool valid = t < n;
+  for (int x = t; x < 6 * kMaskWaves * kOrderKeys; x += kMaskThreads) (&s_cnt[0][0][0])[x] = 0;
+  if (valid) flags[s * n + t] = 0;
+  if (t == 0) n_literal[s] = 0;
+  int len[6] = {0, 0, 0, 0, 0, 0};
+  if (valid) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const uint8_t *m = blocks + (s * 3 + k) * (int64_t)n * n;
+      for (int j = 0; j <= t; ++j) len[k] += block_kept(m, n, t, j) ? 1 : 0;
+      for (int i = t; i < n; ++i) len[3 + k] += block_kept(m, n, i, t) ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  lengths_to_lists(len, n, s, batch, row_ptr, col_ptr, n_edges, sched, s_start, s_wave, s_cnt);
+  if (valid) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const uint8_t *m = blocks + (s * 3 + k) * (int64_t)n * n;
+      int32_t *rows = col_idx + (s * 3 + k) * cap + s_start[k][t];
+      int e = 0;
+      for (int j = 0; j <= t; ++j)
+        if (block_kept(m, n, t, j)) rows[e++] = j;
+      int32_t *cols = row_idx + (s * 3 + k) * cap + s_start[3 + k][t];
+      e = 0;
+      for (int i = t; i < n; ++i)
+        if (block_kept(m, n, i, t)) cols[e++] = i;
+    }
+  }
+}
+
+// BigBird-style fixed block mask, causal form, into class 0 of u8 [B, 3, N, N] (classes 1
+// and 2 get the diagonal only): query block i keeps j <= i when j is within the window
+// (i - j <= w), j is a global block (j < g), i is a global block (i < g, which then sees
+// every earlier block), or j is one of the r random blocks drawn for row i.
+__global__ __launch_bounds__(256) void bigbird_kernel(int64_t batch, int n, int w, int g, int r,
+                                                      const int32_t *__restrict__ rnd,
+                                                      uint8_t *__restrict__ blocks) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_sample = 3 * (int64_t)n * n;
+  if (idx >= batch * per_sample) return;
+  const int64_t s = idx / per_sample;
+  const int64_t rem = idx % per_sample;
+  const int k = (int)(rem / ((int64_t)n * n));
+  const int i = (int)((rem / n) % n), j = (int)(rem % n);
+  bool keep = j == i;
+  if (k == 0 && j <= i) {
+    keep = i - j <= w || j < g || i < g;
+    const int32_t *ri = rnd + (s * n + i) * (int64_t)r;
+    for (int q = 0; q < r && !keep; ++q) keep = ri[q] == j;
+  }
+  blocks[idx] = keep ? 1 : 0;
 }
 
 // base[list][s][k][key] from hist: one workgroup per list.  Segments (s, k) weigh their
@@ -396,6 +488,20 @@ __global__ __launch_bounds__(256) void order_scatter_kernel(const int32_t *__res
 
 }  // namespace
 
+static gsa_status launch_order(const gsa_mask &m, hipStream_t stream) {
+  const int n = m.n_blocks;
+  const int64_t items = m.batch * (int64_t)(m.n_heads[0] + m.n_heads[1] + m.n_heads[2]) * n;
+  if (items == 0) return GSA_OK;
+  hipLaunchKernelGGL(order_base_kernel, dim3(2), dim3(kOrderThreads), 0, stream, m.batch, m.n_heads[0],
+                     m.n_heads[1], m.n_heads[2], m.sched);
+  gsa_status st = check_launch("order_base_kernel");
+  if (st != GSA_OK) return st;
+  hipLaunchKernelGGL(order_scatter_kernel, dim3((unsigned)((items + 255) / 256), 2), dim3(256), 0, stream,
+                     m.sched, m.batch, n, m.n_heads[0], m.n_heads[1], m.n_heads[2], m.row_ptr, m.col_idx,
+                     m.col_ptr, m.row_idx, mask_cap(n), m.work_row, m.work_col);
+  return check_launch("order_scatter_kernel");
+}
+
 gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t stream) {
   const int n = m.n_blocks;
   hipLaunchKernelGGL(mask_kernel, dim3((unsigned)m.batch), dim3(kMaskThreads), 0, stream, c, n,
@@ -403,16 +509,25 @@ gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t st
                      m.n_edges, mask_cap(n), m.sched, m.batch);
   gsa_status st = check_launch("mask_kernel");
   if (st != GSA_OK) return st;
-  const int64_t items = m.batch * (int64_t)(m.n_heads[0] + m.n_heads[1] + m.n_heads[2]) * n;
-  if (items == 0) return GSA_OK;
-  hipLaunchKernelGGL(order_base_kernel, dim3(2), dim3(kOrderThreads), 0, stream, m.batch, m.n_heads[0],
-                     m.n_heads[1], m.n_heads[2], m.sched);
-  st = check_launch("order_base_kernel");
+  return launch_order(m, stream);
+}
+
+gsa_status launch_mask_from_blocks(const uint8_t *blocks, const gsa_mask &m, hipStream_t stream) {
+  const int n = m.n_blocks;
+  hipLaunchKernelGGL(blocks_kernel, dim3((unsigned)m.batch), dim3(kMaskThreads), 0, stream, blocks, n, m.flags,
+                     m.n_literal, m.row_ptr, m.col_idx, m.col_ptr, m.row_idx, m.n_edges, mask_cap(n), m.sched,
+                     m.batch);
+  gsa_status st = check_launch("blocks_kernel");
   if (st != GSA_OK) return st;
-  hipLaunchKernelGGL(order_scatter_kernel, dim3((unsigned)((items + 255) / 256), 2), dim3(256), 0, stream,
-                     m.sched, m.batch, n, m.n_heads[0], m.n_heads[1], m.n_heads[2], m.row_ptr, m.col_idx,
-                     m.col_ptr, m.row_idx, mask_cap(n), m.work_row, m.work_col);
-  return check_launch("order_scatter_kernel");
+  return launch_order(m, stream);
+}
+
+gsa_status launch_bigbird(int64_t batch, int32_t n, int32_t window, int32_t n_global, int32_t n_random,
+                          const int32_t *rnd, uint8_t *blocks, hipStream_t stream) {
+  const int64_t total = batch * 3 * (int64_t)n * n;
+  hipLaunchKernelGGL(bigbird_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, batch, n, window,
+                     n_global, n_random, rnd, blocks);
+  return check_launch("bigbird_kernel");
 }
 
 }  // namespace gsa

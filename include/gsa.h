@@ -170,6 +170,31 @@ gsa_status gsa_mask_sizes(int64_t batch, int32_t n_blocks, const int32_t n_heads
 gsa_status gsa_build_mask(const int32_t *c_dev, const gsa_mask *m, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * (2b) Lists of a caller-given block mask, for comparisons with other block-sparse
+ *      patterns through the same attention kernels (the pages compare the method with
+ *      BigBird: [note] 论文离线与线上效果).
+ *
+ *   blocks_dev  device, uint8 [B, 3, N, N]: nonzero (s, k, i, j) = query block i of class
+ *               k keeps kv-block j.  Entries with j > i are ignored and (i, i) is always
+ *               kept (causal blocks, as for the gzip mask).
+ *   m           as for gsa_build_mask (same buffers and sizes); flags and n_literal are
+ *               set to zero, the lists, counts and work descriptors follow the mask.
+ * Errors as gsa_build_mask; NULL blocks_dev -> GSA_ERR_ARG.  Asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------ */
+gsa_status gsa_build_mask_from_blocks(const uint8_t *blocks_dev, const gsa_mask *m, hipStream_t stream);
+
+/* BigBird-style fixed block mask (causal form) into class 0 of blocks_dev u8 [B, 3, N, N];
+ * classes 1 and 2 get the diagonal only.  Query block i keeps j <= i when i - j <= window,
+ * j < n_global, i < n_global, or j is one of the n_random entries random_dev[s, i, :]
+ * (device int32 [B, N, n_random], each in 0..i; drawn by the caller).  The pages do not
+ * give BigBird's parameters; callers choose them.
+ * Errors: negative batch/window/n_global/n_random -> GSA_ERR_ARG; N outside
+ * 1..GSA_MAX_BLOCKS -> GSA_ERR_UNSUPPORTED; NULL buffers -> GSA_ERR_ARG. */
+gsa_status gsa_bigbird_blocks(int64_t batch, int32_t n_blocks, int32_t window, int32_t n_global,
+                              int32_t n_random, const int32_t *random_dev, uint8_t *blocks_dev,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * (3) Forward: O = softmax(scale Q K^T restricted to the kept set) V per head.
  *     [note] 核心公式 second display: head h of class k(h), query block i attends the
  *     kv-blocks j of its CSR row; inside the diagonal block only keys u <= t are kept;

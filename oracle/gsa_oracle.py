@@ -165,6 +165,38 @@ def default_head_counts(heads: int):
     return (n_local, n_literal, heads - n_local - n_literal)
 
 
+def bigbird_block_mask(n: int, window: int, n_global: int, picks) -> np.ndarray:
+    """BigBird-style causal block mask (the baseline the pages compare against in
+    [note] 论文离线与线上效果; its parameters are not on the pages, so they are inputs).
+
+    Query block i keeps key block j <= i when j is in the window (i - j <= window), j is
+    a global block (j < n_global), i is a global block (i < n_global: it sees every
+    earlier block), or j is one of row i's random picks ``picks[i]``.  Set logic.
+    """
+    out = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        keep = set(range(max(0, i - window), i + 1))
+        keep |= set(range(min(n_global, i + 1)))
+        if i < n_global:
+            keep |= set(range(i + 1))
+        keep |= {int(j) for j in picks[i] if 0 <= int(j) <= i}
+        for j in keep:
+            out[i, j] = True
+    return out
+
+
+def bigbird_masks(picks, window: int, n_global: int) -> np.ndarray:
+    """bool [B, 3, N, N]: class 0 the BigBird-style mask of each sample's picks [N, r],
+    classes 1 and 2 the diagonal only (every head of a BigBird run is class 0)."""
+    picks = np.asarray(picks)
+    batch, n = picks.shape[0], picks.shape[1]
+    out = np.zeros((batch, 3, n, n), dtype=bool)
+    for s in range(batch):
+        out[s, 0] = bigbird_block_mask(n, window, n_global, picks[s])
+        out[s, 1] = out[s, 2] = np.eye(n, dtype=bool)
+    return out
+
+
 def head_classes(n_heads) -> list:
     """Class of every head, contiguous in the order local | literal | hybrid."""
     return [LOCAL] * n_heads[0] + [LITERAL] * n_heads[1] + [HYBRID] * n_heads[2]

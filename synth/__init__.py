@@ -24,7 +24,7 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-STREAM_BYTES, STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_TABLE = range(6)
+STREAM_BYTES, STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_TABLE, STREAM_PICKS = range(7)
 
 # 96 symbols: the 95 printable ASCII characters 0x20..0x7E plus '\n'.
 ALPHABET = np.array([0x0A] + list(range(0x20, 0x7F)), dtype=np.uint8)
@@ -221,3 +221,13 @@ def dense_causal(wl: Workload) -> Workload:
     """The same shape as ``wl`` with every head local and a window covering the whole
     sequence: the mask is then the full causal triangle (dense causal attention)."""
     return replace(wl, name=wl.name + "-dense", window=wl.n_blocks - 1, n_heads=(wl.heads, 0, 0))
+
+
+def bigbird_picks(wl: Workload, n_random: int, batch: int | None = None, n_blocks: int | None = None) -> np.ndarray:
+    """int32 [B, N, r]: the random key blocks of a BigBird-style mask, row i's picks
+    uniform on 0..i (seeded stream 6 of the workload)."""
+    batch = wl.batch if batch is None else batch
+    n = wl.n_blocks if n_blocks is None else n_blocks
+    rng = rng_for(wl.seed_id, STREAM_PICKS)
+    hi = np.arange(1, n + 1)[None, :, None]
+    return (rng.random((batch, n, n_random)) * hi).astype(np.int32)

@@ -40,13 +40,11 @@ def expected_work(masks, n_heads, by_columns: bool):
     return np.argsort(-key, kind="stable").astype(np.int64)
 
 
-def check_mask(m: gsa.GsaMask, c: np.ndarray, block: int, window: int, n_heads):
-    """Bit-exact comparison of every mask buffer with the oracle."""
-    flags, n_lit, masks, csr, csc = expected_mask(c, block, window)
-    b, n = c.shape
+def check_lists(m: gsa.GsaMask, masks: np.ndarray, n_heads):
+    """Bit-exact comparison of the lists, edge counts and work descriptors of ``m`` with
+    the oracle's lists of the block masks ``masks`` bool [B, 3, N, N]."""
+    b, _, n, _ = masks.shape
     cap = n * (n + 1) // 2
-    assert np.array_equal(m.flags.cpu().numpy().reshape(b, n), flags.astype(np.uint8))
-    assert np.array_equal(m.n_literal.cpu().numpy()[:b], n_lit)
     row_ptr = m.row_ptr.cpu().numpy().reshape(b, 3, n + 1)
     col_ptr = m.col_ptr.cpu().numpy().reshape(b, 3, n + 1)
     col_idx = m.col_idx.cpu().numpy().reshape(b, 3, cap)
@@ -54,8 +52,8 @@ def check_mask(m: gsa.GsaMask, c: np.ndarray, block: int, window: int, n_heads):
     n_edges = m.n_edges.cpu().numpy().reshape(b, 3)
     for s in range(b):
         for k in range(3):
-            rp, ci = csr[s][k]
-            cp, ri = csc[s][k]
+            rp, ci = oracle.to_csr(masks[s, k])
+            cp, ri = oracle.to_csc(masks[s, k])
             assert np.array_equal(row_ptr[s, k], rp), (s, k)
             assert np.array_equal(col_idx[s, k, :rp[-1]], ci), (s, k)
             assert np.array_equal(col_ptr[s, k], cp), (s, k)
@@ -73,6 +71,15 @@ def check_mask(m: gsa.GsaMask, c: np.ndarray, block: int, window: int, n_heads):
             assert np.array_equal(desc[:, 1], ptr[s_, k_, i_]), name
             assert np.array_equal(desc[:, 2], ptr[s_, k_, i_ + 1]), name
             assert np.array_equal(desc[:, 3], idx[s_, k_, desc[:, 1]]), name
+
+
+def check_mask(m: gsa.GsaMask, c: np.ndarray, block: int, window: int, n_heads):
+    """Bit-exact comparison of every mask buffer with the oracle."""
+    flags, n_lit, masks, _, _ = expected_mask(c, block, window)
+    b, n = c.shape
+    assert np.array_equal(m.flags.cpu().numpy().reshape(b, n), flags.astype(np.uint8))
+    assert np.array_equal(m.n_literal.cpu().numpy()[:b], n_lit)
+    check_lists(m, masks, n_heads)
     return masks
 
 
