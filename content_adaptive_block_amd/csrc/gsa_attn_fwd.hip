@@ -154,10 +154,11 @@ struct FwdPolicy {
 };
 
 template <typename T, int BLK, int HD>
-// At head_dim <= 64 the kernel is asked to fit five waves per SIMD (<= 96 VGPRs): the
-// three-tile ring lets five workgroups share a CU's LDS, and registers must not be the
-// tighter limit.
-__global__ __launch_bounds__((BLK / (16 * fwd_groups<T, BLK, HD>()) * 64), (HD <= 64 ? 5 : 1)) void attn_fwd_kernel(
+// At head_dim <= 64 the kernel is asked to fit five waves per SIMD (<= 96 VGPRs; three
+// with two row groups per wave): the three-tile ring lets five or six workgroups share a
+// CU's LDS, and registers must not be the tighter limit.
+__global__ __launch_bounds__((BLK / (16 * fwd_groups<T, BLK, HD>()) * 64),
+                             (HD <= 64 ? (fwd_groups<T, BLK, HD>() == 1 ? 5 : 3) : 1)) void attn_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
     float *__restrict__ lse, WorkLists wl, float sl2) {
   constexpr int R = fwd_groups<T, BLK, HD>();

@@ -281,3 +281,45 @@ def test_dense_causal_sampled(inst, batch, n, heads):
         got = np.concatenate([p[0].ravel() for p in pairs])
         ref = np.concatenate([p[1].ravel() for p in pairs])
         assert_close(f"{nm} ({len(pairs)} sampled blocks)", got, ref, ltol if nm == "LSE" else tol)
+
+
+def test_maximum_blocks_sampled():
+    """N = GSA_MAX_BLOCKS (1024 blocks of 64 bytes, 64 KiB per sample) through the bf16
+    instance, checked on sampled query and key blocks."""
+    inst = ("bf16", 64, 64)
+    n, heads, n_heads, window = 1024, 3, (1, 1, 1), 2
+    log(f"  maximum N={n}")
+    x, t = _inputs(inst, 1, n, heads)
+    res = run_path(x, 64, window, n_heads, t, backward=True)
+    masks = check_mask(res["mask"], res["c"], 64, window, n_heads)
+    classes = oracle.head_classes(n_heads)
+    rng = np.random.default_rng(7)
+    errs = {}
+    for h in range(heads):
+        q, k, v, do = (f64(t[nm][0, h]) for nm in ("q", "k", "v", "do"))
+        bm = masks[0, classes[h]]
+        for i in sorted({0, n - 1, int(rng.integers(n))}):
+            rows = np.arange(i * 64, (i + 1) * 64)
+            ro, rl = oracle.attn_fwd_rows(q, k, v, bm, 64, rows)
+            errs.setdefault("O", []).append((f64(res["o"][0, h, rows]), ro))
+            errs.setdefault("LSE", []).append((f64(res["lse"][0, h, rows]), rl))
+            errs.setdefault("dQ", []).append((f64(res["dq"][0, h, rows]), oracle.attn_bwd_qblock(q, k, v, do, bm, 64, i)))
+        lens = bm.sum(axis=0)
+        for j in sorted({n - 1, int(np.argmin(np.where(lens > 1, lens, 10 ** 9)))}):
+            rows = np.arange(j * 64, (j + 1) * 64)
+            rk, rv = oracle.attn_bwd_kblock(q, k, v, do, bm, 64, j)
+            errs.setdefault("dK", []).append((f64(res["dk"][0, h, rows]), rk))
+            errs.setdefault("dV", []).append((f64(res["dv"][0, h, rows]), rv))
+    for nm, pairs in errs.items():
+        got = np.concatenate([p[0].ravel() for p in pairs])
+        ref = np.concatenate([p[1].ravel() for p in pairs])
+        assert_close(f"{nm} ({len(pairs)} sampled blocks)", got, ref, 1e-3 if nm == "LSE" else BF16_TOL)
+
+
+def test_empty_batch_is_a_no_op():
+    q = torch.empty((0, 2, 128, 64), dtype=torch.bfloat16, device="cuda")
+    m = gsa.gsa_build_mask(torch.empty((0, 2), dtype=torch.int32, device="cuda"), 1, (1, 1, 0))
+    o, lse = gsa.gsa_attn_fwd(q, q, q, m, 64)
+    dq, dk, dv = gsa.gsa_attn_bwd(q, q, q, o, lse, q, m, 64)
+    torch.cuda.synchronize()
+    assert o.shape == q.shape and dq.shape == q.shape
