@@ -96,6 +96,16 @@ struct DkdvPolicy {
       const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key0 + 16 * kg;
       S::load_row_frag(kf[kg], k + key_row * HD, g);
       S::load_row_frag(vf[kg], v + key_row * HD, g);
+      // -V: dP is then formed as D - dP on the matrix core (accumulator starting at D),
+      // so no per-block negation is needed; dK's final scale absorbs the sign.
+#pragma unroll
+      for (int ks = 0; ks < S::kKS; ++ks) {
+        if constexpr (S::kBf16) {
+          vf[kg].f[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vf[kg].f[ks]) ^ 0x80008000u);
+        } else {
+          vf[kg].f[ks] = -vf[kg].f[ks];
+        }
+      }
     }
   }
   __device__ void begin(const Item &) {
@@ -133,20 +143,29 @@ struct DkdvPolicy {
 #pragma unroll
       for (int t = 0; t < S::kPartTiles; ++t) {
         const int qb = part * S::kPartTiles + t;
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ll + qb * 16 + 4 * g);
+        const f32x4 l2 = *reinterpret_cast<const f32x4 *>(ll + qb * 16 + 4 * g) * kLog2e;
         const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ld + qb * 16 + 4 * g);
-        f32x4 st[R], dpd[R];   // dpd = dP - D: the product starts from -D
+        f32x4 st[R], dpd[R];   // dpd = D - dP: -V against dO^T, starting from D
         S::template dot_rows_n<R>(lq, qb * 16 + c, g, kf, st);
-        S::template dot_rows_n<R>(ldo, qb * 16 + c, g, vf, dpd, -d4);
+        S::template dot_rows_n<R>(ldo, qb * 16 + c, g, vf, dpd, d4);
 #pragma unroll
         for (int kg = 0; kg < R; ++kg)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float pr = fast_exp2(fmaf(st[kg][r], sl2, -l4[r] * kLog2e));
-            if (diag && key0 + 16 * kg > qb * 16 + 4 * g + r) pr = 0.f;
+            const float pr = fast_exp2(fmaf(st[kg][r], sl2, -l2[r]));
             p[kg][t][r] = pr;
-            ds[kg][t][r] = pr * dpd[kg][r];
+            ds[kg][t][r] = pr * dpd[kg][r];   // -dS
           }
+        if (diag) {   // token-causal mask, diagonal block only
+#pragma unroll
+          for (int kg = 0; kg < R; ++kg)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (key0 + 16 * kg > qb * 16 + 4 * g + r) {
+                p[kg][t][r] = 0.f;
+                ds[kg][t][r] = 0.f;
+              }
+        }
       }
       S::template accumulate_part_n<R>(&dv_acc[0][0], ldo, &p[0][0], S::kPartTiles, part, c, g);
       S::template accumulate_part_n<R>(&dk_acc[0][0], lq, &ds[0][0], S::kPartTiles, part, c, g);
@@ -161,7 +180,7 @@ struct DkdvPolicy {
       T *dvr = dv + key_row * HD;
 #pragma unroll
       for (int db = 0; db < S::kDB; ++db) {
-        S::store4(dkr + db * 16 + 4 * g, dk_acc[kg][db] * scale);
+        S::store4(dkr + db * 16 + 4 * g, dk_acc[kg][db] * -scale);   // the sum holds -dK / scale
         S::store4(dvr + db * 16 + 4 * g, dv_acc[kg][db]);
       }
     }
@@ -265,10 +284,11 @@ struct DqPolicy {
         const f32x4 st = S::dot_rows(lk, kb * 16 + c, g, qf);
         const f32x4 dpd = S::dot_rows(lv, kb * 16 + c, g, dof, f32x4{-dd, -dd, -dd, -dd});   // dP - D
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float pr = fast_exp2(fmaf(st[r], sl2, -lse2));
-          if (diag && kb * 16 + 4 * g + r > q_in_blk) pr = 0.f;
-          ds[t][r] = pr * dpd[r];
+        for (int r = 0; r < 4; ++r) ds[t][r] = fast_exp2(fmaf(st[r], sl2, -lse2)) * dpd[r];
+        if (diag) {   // token-causal mask, diagonal block only
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb * 16 + 4 * g + r > q_in_blk) ds[t][r] = 0.f;
         }
       }
       S::accumulate_part(acc, lk, ds, part, c, g);
