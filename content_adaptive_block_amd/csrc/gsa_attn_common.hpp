@@ -53,7 +53,7 @@ struct WorkLists {
   int heads, n, n_loc, n_lit;
   int64_t cap;
   __device__ __forceinline__ WorkItem decode(int64_t pos) const {
-    const u32x4 d = reinterpret_cast<const u32x4 *>(work)[pos];
+    const u32x4 d = load_uniform(reinterpret_cast<const u32x4 *>(work) + pos);
     WorkItem it;
     const uint32_t item = d[0];
     it.blk = (int)(item % (uint32_t)n);
@@ -311,7 +311,7 @@ __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
   int stage = 0;
   for (int e = it.beg; e < it.end; ++e) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
+    wg_barrier();
     const int nx = e + 1 - (it.beg + 1);   // position of entry e + 1 after the first
     if (e + 1 < it.end) {
       if (nx > 0 && (nx & (kWave - 1)) == 0)
@@ -348,7 +348,7 @@ __device__ __forceinline__ void run_item_ring(P &pol, const WorkItem &it) {
   pol.begin(it);
   for (int e = it.beg; e < it.end; ++e) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
+    wg_barrier();
     const int nx_pos = e - it.beg;   // entry e + 1 sits at this position of the chunk run
     const bool more = e + 1 < it.end;
     int j_next = 0;
@@ -359,7 +359,7 @@ __device__ __forceinline__ void run_item_ring(P &pol, const WorkItem &it) {
       pol.copy_k(it, j_next, spare);
     }
     pol.compute_a(it, e, ks, vs);
-    __syncthreads();
+    wg_barrier();
     const int freed = P::kFreeK ? ks : vs;
     if (more) pol.copy_v(it, j_next, freed);
     pol.compute_b(it, e, ks, vs);

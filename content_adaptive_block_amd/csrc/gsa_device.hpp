@@ -80,5 +80,27 @@ __device__ __forceinline__ void copy4_to_lds(const void *g, unsigned char *lds_w
 // s_waitcnt immediate for "vmcnt <= n" leaving the other counters alone (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kLgkmZero = 15 | (7 << 4) | (0 << 8) | (3 << 14);   // "lgkmcnt <= 0" only
+
+// Workgroup barrier for the copy pipelines.  __syncthreads() is a release fence, and the
+// compiler counts asynchronous global -> LDS copies as pending LDS stores, so it drains
+// every copy in flight (vmcnt(0)) at each one, which defeats prefetching.  Here the
+// callers wait for the copies they need with explicit vmcnt counts; the barrier only
+// finishes this wave's LDS accesses and stops the compiler from moving memory accesses
+// across it (a compiler-only fence emits no instruction).
+__device__ __forceinline__ void wg_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kLgkmZero);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Read of a value that no thread of the kernel writes, at a wave-uniform address.  Through
+// the constant address space it becomes a scalar load (counted by lgkmcnt, so waiting for
+// it does not wait for the vector loads and copies in flight).
+template <typename V>
+__device__ __forceinline__ V load_uniform(const V *p) {
+  return *(const __attribute__((address_space(4))) V *)p;
+}
 
 }  // namespace gsa
