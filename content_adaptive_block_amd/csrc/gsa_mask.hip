@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_base_kernel(int64_t batch
   const int32_t *hist = sched + list * nseg * kOrderKeys;
   int32_t *base = sched + (2 + list) * nseg * kOrderKeys;
   int v[kOrderKeys];
-  // Items per key over every segment (the first chunk's counts stay in registers).
+  // Items per key over every segment (with a single chunk its counts stay in registers).
   int tot[kOrderKeys] = {};
   for (int64_t c0 = 0; c0 < nseg; c0 += kOrderThreads) {
     load_counts(hist, c0 + t, nseg, nh, v);
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_base_kernel(int64_t batch
   // Exclusive scan over segments, per key, one chunk of segments at a time.
   for (int64_t c0 = 0; c0 < nseg; c0 += kOrderThreads) {
     const int64_t seg = c0 + t;
-    if (c0 > 0) load_counts(hist, seg, nseg, nh, v);
+    if (nseg > kOrderThreads) load_counts(hist, seg, nseg, nh, v);
     int incl[kOrderKeys];
 #pragma unroll
     for (int kk = 0; kk < kOrderKeys; ++kk) incl[kk] = v[kk];
@@ -486,12 +486,93 @@ __global__ __launch_bounds__(256) void order_scatter_kernel(const int32_t *__res
       u32x4{(uint32_t)idx, (uint32_t)beg, (uint32_t)end, (uint32_t)first};
 }
 
+// order_base_kernel and order_scatter_kernel in one launch, for batches whose per-list
+// histograms fit in LDS: every workgroup loads the histogram of its list and forms the
+// bases itself (a few hundred counts), which costs less than a kernel boundary.
+constexpr int kFusedMaxBatch = 128;
+constexpr int kFusedMaxSeg = 3 * kFusedMaxBatch;
+
+__global__ __launch_bounds__(kOrderThreads) void order_fused_kernel(const int32_t *__restrict__ sched, int64_t batch,
+                                                                    int n, int n_loc, int n_lit, int n_hyb,
+                                                                    const int32_t *__restrict__ row_ptr,
+                                                                    const int32_t *__restrict__ col_idx,
+                                                                    const int32_t *__restrict__ col_ptr,
+                                                                    const int32_t *__restrict__ row_idx, int64_t cap,
+                                                                    int32_t *__restrict__ work_row,
+                                                                    int32_t *__restrict__ work_col) {
+  static_assert(kOrderThreads == kOrderKeys * 16, "16 chunks of segments per key");
+  __shared__ int s_pre[kFusedMaxSeg][kOrderKeys];   // weighted counts, then exclusive prefixes
+  __shared__ int s_chunk[16][kOrderKeys], s_tot[kOrderKeys], s_first[kOrderKeys];
+  const int t = threadIdx.x;
+  const int list = blockIdx.y;
+  const int nseg = (int)(3 * batch);
+  const int nh[3] = {n_loc, n_lit, n_hyb};
+  const int32_t *hist = sched + (int64_t)list * nseg * kOrderKeys;
+  for (int x = t; x < nseg * kOrderKeys; x += kOrderThreads)
+    s_pre[x / kOrderKeys][x % kOrderKeys] = nh[(x / kOrderKeys) % 3] * hist[x];
+  __syncthreads();
+  // Thread (chunk, key): segments [lo, hi) of one key.
+  const int key = t % kOrderKeys, chunk = t / kOrderKeys;
+  const int per = (nseg + 15) / 16;
+  const int lo = min(chunk * per, nseg), hi = min(lo + per, nseg);
+  int sum = 0;
+  for (int sg = lo; sg < hi; ++sg) sum += s_pre[sg][key];
+  s_chunk[chunk][key] = sum;
+  __syncthreads();
+  int run = 0, total = 0;
+  for (int c2 = 0; c2 < 16; ++c2) {
+    const int v = s_chunk[c2][key];
+    if (c2 < chunk) run += v;
+    total += v;
+  }
+  for (int sg = lo; sg < hi; ++sg) {
+    const int v = s_pre[sg][key];
+    s_pre[sg][key] = run;
+    run += v;
+  }
+  if (chunk == 0) s_tot[key] = total;
+  __syncthreads();
+  if (t < kOrderKeys) {
+    int first = 0;
+    for (int k2 = t + 1; k2 < kOrderKeys; ++k2) first += s_tot[k2];
+    s_first[t] = first;
+  }
+  __syncthreads();
+
+  const int heads = n_loc + n_lit + n_hyb;
+  const int64_t items = batch * heads * (int64_t)n;
+  const int64_t idx = (int64_t)blockIdx.x * kOrderThreads + t;
+  if (idx >= items) return;
+  const int i = (int)(idx % n);
+  const int64_t sh = idx / n;
+  const int h = (int)(sh % heads);
+  const int64_t s = sh / heads;
+  const int k = h < n_loc ? 0 : (h < n_loc + n_lit ? 1 : 2);
+  const int h0 = k == 0 ? 0 : (k == 1 ? n_loc : n_loc + n_lit);
+  const int seg = (int)(s * 3 + k);
+  const int32_t pk = sched[4 * batch * 3 * kOrderKeys + ((int64_t)list * nseg + seg) * n + i];
+  const int32_t *ptr = (list == 0 ? row_ptr : col_ptr) + seg * (int64_t)(n + 1);
+  const int beg = ptr[i], end = ptr[i + 1];
+  const int first = (list == 0 ? col_idx : row_idx)[seg * cap + beg];
+  const int kk = pk & 15;
+  const int64_t pos = s_first[kk] + s_pre[seg][kk] + (int64_t)(h - h0) * hist[seg * kOrderKeys + kk] + (pk >> 4);
+  reinterpret_cast<u32x4 *>(list == 0 ? work_row : work_col)[pos] =
+      u32x4{(uint32_t)idx, (uint32_t)beg, (uint32_t)end, (uint32_t)first};
+}
+
 }  // namespace
 
 static gsa_status launch_order(const gsa_mask &m, hipStream_t stream) {
   const int n = m.n_blocks;
   const int64_t items = m.batch * (int64_t)(m.n_heads[0] + m.n_heads[1] + m.n_heads[2]) * n;
   if (items == 0) return GSA_OK;
+  if (m.batch <= kFusedMaxBatch) {
+    hipLaunchKernelGGL(order_fused_kernel, dim3((unsigned)((items + kOrderThreads - 1) / kOrderThreads), 2),
+                       dim3(kOrderThreads), 0, stream, m.sched, m.batch, n, m.n_heads[0], m.n_heads[1],
+                       m.n_heads[2], m.row_ptr, m.col_idx, m.col_ptr, m.row_idx, mask_cap(n), m.work_row,
+                       m.work_col);
+    return check_launch("order_fused_kernel");
+  }
   hipLaunchKernelGGL(order_base_kernel, dim3(2), dim3(kOrderThreads), 0, stream, m.batch, m.n_heads[0],
                      m.n_heads[1], m.n_heads[2], m.sched);
   gsa_status st = check_launch("order_base_kernel");

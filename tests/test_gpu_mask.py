@@ -54,6 +54,19 @@ def test_mask_size_patterns(n):
             check_mask(m, c, 64, window, heads)
 
 
+@pytest.mark.parametrize("batch", [127, 128, 129, 200])
+def test_mask_batch_sizes(batch):
+    # the work order is built in one launch while a list's histogram fits in LDS (up to
+    # 128 samples) and in two above that; both must give the same descriptors
+    rng = np.random.default_rng(batch)
+    c = rng.integers(20, 90, (batch, 9)).astype(np.int32)
+    c[::7] = 40                                   # some samples without literal blocks
+    log(f"  mask B={batch} N=9")
+    m = gsa.gsa_build_mask(torch.from_numpy(c).cuda(), 1, (2, 1, 1))
+    torch.cuda.synchronize()
+    check_mask(m, c, 64, 1, (2, 1, 1))
+
+
 @pytest.mark.parametrize("heads", [(4, 0, 0), (0, 3, 0), (0, 0, 2), (0, 0, 0), (3, 1, 5)])
 def test_mask_head_splits(heads):
     rng = np.random.default_rng(9)
