@@ -79,6 +79,9 @@ EDGE = [
     ("literal-only", ("bf16", 64, 64), 2, 10, (0, 2, 0), 2, None),
     ("hybrid-only", ("f32", 16, 32), 1, 12, (0, 0, 3), 1, None),
     ("one-head", ("f32", 16, 32), 3, 5, (1, 0, 0), 1, None),
+    # more than 128 samples: the work order takes its two-launch path
+    ("many-samples-f32", ("f32", 16, 32), 130, 3, (1, 1, 1), 1, None),
+    ("many-samples-bf16", ("bf16", 64, 64), 140, 2, (1, 0, 1), 1, None),
 ]
 
 
