@@ -105,6 +105,40 @@ def test_edge_cases(name, inst, batch, n, n_heads, window, bytes_kind):
         assert_close(nm, f64(res[nm]), ref, tol)
 
 
+def _random_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    inst = list(BASE)[seed % 3]
+    n_max = {16: 70, 64: 40, 128: 16}[inst[1]]
+    batch, n = int(rng.integers(1, 4)), int(rng.integers(1, n_max + 1))
+    n_heads = tuple(int(x) for x in rng.integers(0, 3, 3))
+    if sum(n_heads) == 0:
+        n_heads = (0, 1, 0)
+    return inst, batch, n, n_heads, int(rng.integers(0, 6)), rng
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(seed):
+    # seeded random instance, batch, block count, head split and window; some samples get
+    # constant runs so that their literal sets vary from empty to most blocks
+    inst, batch, n, n_heads, window, rng = _random_case(seed)
+    dtype, block, hd = inst
+    log(f"  random#{seed}: {dtype} b={block} B={batch} N={n} heads={n_heads} w={window}")
+    x, t = _inputs(inst, batch, n, sum(n_heads))
+    for s_ in range(batch):
+        for _ in range(int(rng.integers(0, 3))):
+            a = int(rng.integers(0, n)) * block
+            x[s_, a:a + int(rng.integers(1, 4)) * block] = int(rng.integers(32, 127))
+    res = run_path(x, block, window, n_heads, t, backward=True)
+    masks = check_mask(res["mask"], res["c"], block, window, n_heads)
+    ref_o, ref_lse = oracle.attn_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), masks, n_heads, block)
+    ref_g = oracle.attn_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), masks, n_heads, block)
+    tol, ltol = _tol(dtype)
+    assert_close("O", f64(res["o"]), ref_o, tol)
+    assert_close("LSE", f64(res["lse"]), ref_lse, ltol)
+    for nm, ref in zip(("dq", "dk", "dv"), ref_g):
+        assert_close(nm, f64(res[nm]), ref, tol)
+
+
 def test_row0_is_v0_and_determinism():
     inst = ("bf16", 64, 64)
     x, t = _inputs(inst, 2, 12, 8)
