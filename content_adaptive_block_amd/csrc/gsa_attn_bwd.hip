@@ -16,7 +16,8 @@
 //             one block ahead; Q_i^T and dO_i^T come from transposing LDS reads.
 //   bwd_dq    one workgroup per (sample, head, query block i), walking the CSR row of i;
 //             each wave keeps 16 query rows of Q_i and dO_i in registers and accumulates
-//             dQ^T while K_j and V_j stream the same way (K_j^T by transposing reads).
+//             dQ^T while K_j and V_j stream through a ring of three LDS tiles (V_j's
+//             tile takes V_{j+1} as soon as dS is formed; K_j^T by transposing reads).
 //             It also forms D of its rows from O and dO and writes it for dK/dV, so the
 //             full backward runs dQ, then dK/dV, with no separate pass for D.
 #include <type_traits>
@@ -223,7 +224,7 @@ template <typename T, int BLK, int HD>
 struct DqPolicy {
   using S = AttnShape<T, BLK, HD>;
   using Item = WorkItem;
-  static constexpr int kStageBytes = 2 * S::kTileBytes;
+  static constexpr int kLdsBytes = 3 * S::kTileBytes;   // the ring: K_j, V_j and a spare
 
   const T *q, *k, *v, *o, *dout;
   const float *lse;
@@ -263,36 +264,39 @@ struct DqPolicy {
 #pragma unroll
     for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __device__ void copy(const Item &it, int j, int stage) {
-    const int64_t off = (it.sh * seq + (int64_t)j * BLK) * HD;
-    unsigned char *dst = lds + stage * kStageBytes;
-    S::copy_tile(dst, k + off, tid);
-    S::copy_tile(dst + S::kTileBytes, v + off, tid);
+  static constexpr bool kFreeK = false;   // V_j is done once dS is formed; K_j is read again
+  __device__ void copy_k(const Item &it, int j, int slot) {
+    S::copy_tile(lds + slot * S::kTileBytes, k + (it.sh * seq + (int64_t)j * BLK) * HD, tid);
   }
-  __device__ void compute(const Item &it, int e, int stage) {
-    const unsigned char *lk = lds + stage * kStageBytes;
-    const unsigned char *lv = lk + S::kTileBytes;
+  __device__ void copy_v(const Item &it, int j, int slot) {
+    S::copy_tile(lds + slot * S::kTileBytes, v + (it.sh * seq + (int64_t)j * BLK) * HD, tid);
+  }
+  // dS^T[key][q] of every key of the tile (lane holds keys kb*16 + 4g + r of its query):
+  // S^T from K_j and dP^T - D from V_j.
+  f32x4 dsr[S::kKB];
+  __device__ void compute_a(const Item &it, int e, int k_slot, int v_slot) {
+    const unsigned char *lk = lds + k_slot * S::kTileBytes;
+    const unsigned char *lv = lds + v_slot * S::kTileBytes;
     const bool diag = e == it.end - 1;   // row i ends with its own block j = i
-    // dS^T[key][q], one part of 16*kPartTiles keys at a time: lane holds keys
-    // kb*16 + 4g + r of its query.
 #pragma unroll
-    for (int part = 0; part < S::kParts; ++part) {
-      f32x4 ds[S::kPartTiles];
+    for (int kb = 0; kb < S::kKB; ++kb) {
+      const f32x4 st = S::dot_rows(lk, kb * 16 + c, g, qf);
+      const f32x4 dpd = S::dot_rows(lv, kb * 16 + c, g, dof, f32x4{-dd, -dd, -dd, -dd});   // dP - D
 #pragma unroll
-      for (int t = 0; t < S::kPartTiles; ++t) {
-        const int kb = part * S::kPartTiles + t;
-        const f32x4 st = S::dot_rows(lk, kb * 16 + c, g, qf);
-        const f32x4 dpd = S::dot_rows(lv, kb * 16 + c, g, dof, f32x4{-dd, -dd, -dd, -dd});   // dP - D
+      for (int r = 0; r < 4; ++r) dsr[kb][r] = fast_exp2(fmaf(st[r], sl2, -lse2)) * dpd[r];
+      if (diag) {   // token-causal mask, diagonal block only
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ds[t][r] = fast_exp2(fmaf(st[r], sl2, -lse2)) * dpd[r];
-        if (diag) {   // token-causal mask, diagonal block only
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kb * 16 + 4 * g + r > q_in_blk) ds[t][r] = 0.f;
-        }
+        for (int r = 0; r < 4; ++r)
+          if (kb * 16 + 4 * g + r > q_in_blk) dsr[kb][r] = 0.f;
       }
-      S::accumulate_part(acc, lk, ds, part, c, g);
     }
+  }
+  // dQ^T += K_j^T dS^T, one part of 16*kPartTiles keys at a time.
+  __device__ void compute_b(const Item &, int, int k_slot, int) {
+    const unsigned char *lk = lds + k_slot * S::kTileBytes;
+#pragma unroll
+    for (int part = 0; part < S::kParts; ++part)
+      S::accumulate_part(acc, lk, &dsr[part * S::kPartTiles], part, c, g);
   }
   __device__ void finish(const Item &it) {
     const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk;
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dq_kernel(
     const T *__restrict__ dout, const float *__restrict__ lse, float *__restrict__ dvec, T *__restrict__ dq,
     WorkLists wl, float sl2, float scale) {
   using P = DqPolicy<T, BLK, HD>;
-  __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
+  __shared__ __align__(16) unsigned char lds[P::kLdsBytes];
   const WorkItem it = wl.decode(dispatch_position(blockIdx.x, gridDim.x));
 
   P pol;
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dq_kernel(
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
   pol.q_in_blk = (threadIdx.x >> 6) * 16 + pol.c;
-  run_item(pol, it);
+  run_item_ring(pol, it);
 }
 
 template <typename T, int BLK, int HD>
