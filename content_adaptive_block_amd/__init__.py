@@ -342,6 +342,20 @@ def _check_tensors(*ts):
         raise ValueError("tensors must be [B, H, T, d]")
 
 
+def _check_out(t, ref, name):
+    """An output the caller passes in must be a contiguous tensor like ``ref``."""
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.device == ref.device and t.dtype == ref.dtype
+            and t.shape == ref.shape and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {ref.dtype} tensor {tuple(ref.shape)} on {ref.device}")
+
+
+def _check_rows(t, ref, name):
+    """A per-row fp32 vector [B, H, T] for the tensors shaped like ``ref``."""
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.device == ref.device and t.dtype == torch.float32
+            and t.shape == ref.shape[:3] and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous float32 tensor {tuple(ref.shape[:3])} on {ref.device}")
+
+
 def _fwd_struct(q, k, v, o, lse, block, scale) -> _FwdArgs:
     a = _FwdArgs()
     a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)
@@ -356,8 +370,11 @@ def gsa_attn_fwd(q, k, v, mask: GsaMask, block: int, scale: float = 0.0, with_ls
     """O [B, H, T, d] (and LSE fp32 [B, H, T]) of the gzip-masked causal attention."""
     _check_tensors(q, k, v)
     o = torch.empty_like(q) if out is None else out
+    _check_out(o, q, "out")
     if with_lse and lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if with_lse:
+        _check_rows(lse, q, "lse")
     a = _fwd_struct(q, k, v, o, lse if with_lse else None, block, scale)
     ms = mask.struct()
     _check(load_library().gsa_attn_fwd(ctypes.byref(a), ctypes.byref(ms), _stream_ptr(q.device)),
@@ -382,9 +399,14 @@ def gsa_attn_bwd(q, k, v, o, lse, dout, mask: GsaMask, block: int, scale: float 
     writes D into ``workspace``), then "dkdv" (reads it); "prep" writes D alone, for
     running "dkdv" without "dq".  Stages share ``workspace`` and ``out``."""
     _check_tensors(q, k, v, o, dout)
+    if lse is not None or stage != "prep":   # the D-only stage reads no LSE
+        _check_rows(lse, q, "lse")
     dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_out(t, q, name)
     if workspace is None:
         workspace = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check_rows(workspace, q, "workspace")
     b = _bwd_struct(q, k, v, o, lse, dout, dq, dk, dv, workspace, block, scale)
     ms = mask.struct()
     fn = getattr(load_library(), BWD_STAGES[stage])

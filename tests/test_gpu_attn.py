@@ -353,6 +353,34 @@ def test_maximum_blocks_sampled():
         assert_close(f"{nm} ({len(pairs)} sampled blocks)", got, ref, 1e-3 if nm == "LSE" else BF16_TOL)
 
 
+def test_binding_rejects_mismatched_outputs():
+    # wrong caller-supplied outputs are refused before anything is launched
+    inst = ("bf16", 64, 64)
+    x, t = _inputs(inst, 1, 3, 4)
+    c = gsa.gsa_prepare(x, 64)
+    m = gsa.gsa_build_mask(torch.from_numpy(c).cuda(), 1, (2, 1, 1))
+    q, k, v, do = (t[nm].cuda() for nm in ("q", "k", "v", "do"))
+    o, lse = gsa.gsa_attn_fwd(q, k, v, m, 64)
+    bad = [
+        dict(out=torch.empty_like(q[:, :2])),                                   # fewer heads
+        dict(out=torch.empty_like(q, dtype=torch.float32)),                     # other dtype
+        dict(out=torch.empty_like(q).transpose(2, 3).contiguous().transpose(2, 3)),  # not contiguous
+        dict(lse=torch.empty(q.shape[:3], dtype=torch.bfloat16, device=q.device)),
+        dict(lse=torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            gsa.gsa_attn_fwd(q, k, v, m, 64, **kw)
+    g = tuple(torch.empty_like(q) for _ in range(3))
+    with pytest.raises(ValueError):
+        gsa.gsa_attn_bwd(q, k, v, o, lse, do, m, 64, out=(g[0], g[1], g[2][:, :1]))
+    with pytest.raises(ValueError):
+        gsa.gsa_attn_bwd(q, k, v, o, lse, do, m, 64, workspace=torch.empty(3, device=q.device))
+    with pytest.raises(ValueError):
+        gsa.gsa_attn_bwd(q, k, v, o, None, do, m, 64)
+    torch.cuda.synchronize()
+
+
 def test_empty_batch_is_a_no_op():
     q = torch.empty((0, 2, 128, 64), dtype=torch.bfloat16, device="cuda")
     m = gsa.gsa_build_mask(torch.empty((0, 2), dtype=torch.int32, device="cuda"), 1, (1, 1, 0))
