@@ -275,8 +275,8 @@ def gsa_build_mask(c, window: int, n_heads, device=None, out: GsaMask | None = N
         raise ValueError("c must be [batch, n_blocks]")
     batch, n = c.shape
     m = out if out is not None else GsaMask.empty(batch, n, window, n_heads, device)
-    if (m.batch, m.n_blocks) != (batch, n):
-        raise ValueError("preallocated mask has another shape")
+    if (m.batch, m.n_blocks) != (batch, n) or m.n_heads != tuple(int(h) for h in n_heads):
+        raise ValueError("preallocated mask has another shape or head split")
     m.window = window
     ms = m.struct()
     _check(load_library().gsa_build_mask(c.data_ptr(), ctypes.byref(ms), _stream_ptr(device)),
@@ -293,8 +293,8 @@ def gsa_build_mask_from_blocks(blocks: torch.Tensor, n_heads, out: GsaMask | Non
     blocks = blocks.contiguous()
     batch, n = blocks.shape[0], blocks.shape[2]
     m = out if out is not None else GsaMask.empty(batch, n, 0, n_heads, blocks.device)
-    if (m.batch, m.n_blocks) != (batch, n):
-        raise ValueError("preallocated mask has another shape")
+    if (m.batch, m.n_blocks) != (batch, n) or m.n_heads != tuple(int(h) for h in n_heads):
+        raise ValueError("preallocated mask has another shape or head split")
     m.window = 0
     ms = m.struct()
     _check(load_library().gsa_build_mask_from_blocks(blocks.data_ptr(), ctypes.byref(ms), _stream_ptr(blocks.device)),
