@@ -42,11 +42,13 @@ KERNEL_SOURCES = {"fwd": "gsa_attn_fwd.hip", "bwd_prep": "gsa_attn_bwd.hip", "bw
 
 
 def kernel_source_hash(name: str) -> str:
-    """Hash of the sources a kernel is built from (its file plus the shared headers)."""
+    """Hash of what a kernel is built from: its file, the shared headers and the build
+    script (its compiler flags)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "content_adaptive_block_amd", "csrc")
-    for f in (KERNEL_SOURCES[name], "gsa_attn_common.hpp", "gsa_device.hpp"):
-        with open(os.path.join(csrc, f), "rb") as fh:
+    pkg = os.path.join(ROOT, "content_adaptive_block_amd")
+    for f in (os.path.join("csrc", KERNEL_SOURCES[name]), os.path.join("csrc", "gsa_attn_common.hpp"),
+              os.path.join("csrc", "gsa_device.hpp"), "_build.py"):
+        with open(os.path.join(pkg, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

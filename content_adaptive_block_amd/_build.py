@@ -27,8 +27,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{IN
 # MFMA accumulators stay in ordinary VGPRs (no AGPR copies around every product).
 # -ffast-math includes finite-math: the kernels keep every value finite (a masked score
 # is -1e30, not -inf), so max() needs no NaN canonicalisation.
+# The instruction scheduler favours instruction-level parallelism over register pressure
+# (max-ilp): at the occupancy the kernels ask for it measured 0.5-1.6% faster per kernel.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-ffast-math", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+          "-ffast-math", "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 
 
 def _hipcc() -> str:
