@@ -1,0 +1,90 @@
+"""Host-side arithmetic of bench.py: algorithmic bytes and flops, kept-tile and token-edge
+counts, the HBM-counter scaling, and the one-GPU guard.  No GPU is touched."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_kernel_work_matches_the_tensor_sizes():
+    wl = synth.WORKLOADS[4]                       # 8 x 8192 B, 12 heads, d 64, bf16
+    x = 8 * 12 * 8192 * 64 * 2                    # one [B, H, T, d] bf16 tensor
+    r = 8 * 12 * 8192 * 4                         # one fp32 [B, H, T] vector
+    assert x == 100_663_296 and r == 3_145_728
+    tile = 64 * 64 * 64
+    assert bench.kernel_work("fwd", wl, 10) == (4 * x + r, 4 * tile * 10)
+    assert bench.kernel_work("bwd_dkdv", wl, 10) == (6 * x + 2 * r, 8 * tile * 10)
+    dq_bytes, dq_flops = bench.kernel_work("bwd_dq", wl, 10)
+    assert dq_bytes == 6 * x + 2 * r and dq_flops == 6 * tile * 10 + 2 * 8 * 12 * 8192 * 64
+    # forward + both backward stages count 4 + 6 + 8 = 18 b^2 d per tile of matrix work,
+    # of which the algorithmic 14 (4 forward, 10 backward) enter the headline figure
+    assert bench.kernel_work("fwd", wl, 1)[1] + bench.kernel_work("bwd_dkdv", wl, 1)[1] + \
+        bench.kernel_work("bwd_dq", wl, 1)[1] - 2 * 8 * 12 * 8192 * 64 == 18 * tile
+
+
+def test_kept_tiles_and_token_edges_by_brute_force():
+    rng = np.random.default_rng(3)
+    n, b, n_heads = 7, 4, (2, 1, 3)
+    flags = rng.integers(0, 2, (2, n)).astype(bool)
+    masks = oracle.block_masks(flags, 1)                          # [2, 3, n, n]
+    n_edges = np.array([[int(masks[s, k].sum()) for k in range(3)] for s in range(2)])
+    assert bench.kept_tiles(n_edges, n_heads) == sum(
+        n_heads[k] * int(masks[s, k].sum()) for s in range(2) for k in range(3))
+    tok = 0
+    for s in range(2):
+        for k in range(3):
+            tm = oracle.token_mask(masks[s, k], b)
+            tok += n_heads[k] * int(tm.sum())
+    assert bench.token_edges(n_edges, n_heads, n, b) == tok
+
+
+def _counter_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_pmc_means_average_per_kernel(tmp_path):
+    p = tmp_path / "c.csv"
+    _counter_csv(p, [
+        {"Kernel_Name": "void gsa::attn_fwd_kernel<bf16>(...)", "Counter_Name": "FETCH_SIZE", "Counter_Value": 100},
+        {"Kernel_Name": "void gsa::attn_fwd_kernel<bf16>(...)", "Counter_Name": "FETCH_SIZE", "Counter_Value": 300},
+        {"Kernel_Name": "void gsa::attn_fwd_kernel<bf16>(...)", "Counter_Name": "WRITE_SIZE", "Counter_Value": 7},
+        {"Kernel_Name": "neg_kernel", "Counter_Name": "FETCH_SIZE", "Counter_Value": 512},
+        {"Kernel_Name": "something_else", "Counter_Name": "FETCH_SIZE", "Counter_Value": 9},
+    ])
+    m = bench._pmc_means(str(p), "FETCH_SIZE")
+    assert m["fwd"] == (200.0, 2) and m["copy"] == (512.0, 1) and len(m) == 2
+
+
+def test_gpus_above_one_exit_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("name", ["fwd", "bwd_dq", "bwd_dkdv"])
+def test_traffic_records(name):
+    # a committed record is used only while it matches the kernel's sources and build
+    # flags; its bytes are at least the compulsory ones
+    wl = synth.WORKLOADS[4]
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{wl.name}.json")
+    rec = json.load(open(path))
+    assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
+    compulsory = bench.kernel_work(name, wl, 0)[0]
+    assert compulsory <= rec["bytes_per_launch"] < 2 * compulsory
+    current = rec["source_hash"] == bench.kernel_source_hash(name)
+    assert bench.load_traffic(name, wl) == (float(rec["bytes_per_launch"]) if current else None)
