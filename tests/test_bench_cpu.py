@@ -83,7 +83,7 @@ def test_traffic_records(name):
     wl = synth.WORKLOADS[4]
     path = os.path.join(ROOT, "profiles", f"traffic_{name}_{wl.name}.json")
     rec = json.load(open(path))
-    assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
+    assert abs(rec["bytes_per_launch"] - rec["fetch_bytes"] - rec["write_bytes"]) <= 1   # each rounded
     compulsory = bench.kernel_work(name, wl, 0)[0]
     assert compulsory <= rec["bytes_per_launch"] < 2 * compulsory
     current = rec["source_hash"] == bench.kernel_source_hash(name)
