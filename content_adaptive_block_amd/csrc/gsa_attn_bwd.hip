@@ -222,9 +222,11 @@ __global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64)) void
 // D = rowsum(dO * O) is formed from the rows it loads anyway and written out for dK/dV.
 template <typename T, int BLK, int HD>
 struct DqPolicy {
-  using S = AttnShape<T, BLK, HD>;
+  static constexpr int KC = kv_piece_rows<T, BLK, HD>();
+  using S = AttnShape<T, BLK, HD, 1, KC>;
   using Item = WorkItem;
-  static constexpr int kLdsBytes = 3 * S::kTileBytes;   // the ring: K_j, V_j and a spare
+  static constexpr int kSub = BLK / KC;                  // pieces per kv-block
+  static constexpr int kLdsBytes = 3 * S::kTileBytes;   // the ring: K, V and a spare
 
   const T *q, *k, *v, *o, *dout;
   const float *lse;
@@ -265,16 +267,16 @@ struct DqPolicy {
     for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   static constexpr bool kFreeK = false;   // V_j is done once dS is formed; K_j is read again
-  __device__ void copy_k(const Item &it, int j, int slot) {
-    S::copy_tile(lds + slot * S::kTileBytes, k + (it.sh * seq + (int64_t)j * BLK) * HD, tid);
+  __device__ void copy_k(const Item &it, int j, int piece, int slot) {
+    S::copy_tile(lds + slot * S::kTileBytes, k + (it.sh * seq + (int64_t)j * BLK + piece * KC) * HD, tid);
   }
-  __device__ void copy_v(const Item &it, int j, int slot) {
-    S::copy_tile(lds + slot * S::kTileBytes, v + (it.sh * seq + (int64_t)j * BLK) * HD, tid);
+  __device__ void copy_v(const Item &it, int j, int piece, int slot) {
+    S::copy_tile(lds + slot * S::kTileBytes, v + (it.sh * seq + (int64_t)j * BLK + piece * KC) * HD, tid);
   }
-  // dS^T[key][q] of every key of the tile (lane holds keys kb*16 + 4g + r of its query):
-  // S^T from K_j and dP^T - D from V_j.
+  // dS^T[key][q] of every key of the piece (lane holds keys piece*KC + kb*16 + 4g + r of its
+  // query): S^T from K and dP^T - D from V.
   f32x4 dsr[S::kKB];
-  __device__ void compute_a(const Item &it, int e, int k_slot, int v_slot) {
+  __device__ void compute_a(const Item &it, int e, int piece, int k_slot, int v_slot) {
     const unsigned char *lk = lds + k_slot * S::kTileBytes;
     const unsigned char *lv = lds + v_slot * S::kTileBytes;
     const bool diag = e == it.end - 1;   // row i ends with its own block j = i
@@ -287,12 +289,12 @@ struct DqPolicy {
       if (diag) {   // token-causal mask, diagonal block only
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (kb * 16 + 4 * g + r > q_in_blk) dsr[kb][r] = 0.f;
+          if (piece * KC + kb * 16 + 4 * g + r > q_in_blk) dsr[kb][r] = 0.f;
       }
     }
   }
-  // dQ^T += K_j^T dS^T, one part of 16*kPartTiles keys at a time.
-  __device__ void compute_b(const Item &, int, int k_slot, int) {
+  // dQ^T += K^T dS^T over the piece, one part of 16*kPartTiles keys at a time.
+  __device__ void compute_b(const Item &, int, int, int k_slot, int) {
     const unsigned char *lk = lds + k_slot * S::kTileBytes;
 #pragma unroll
     for (int part = 0; part < S::kParts; ++part)
@@ -307,7 +309,7 @@ struct DqPolicy {
 };
 
 template <typename T, int BLK, int HD>
-__global__ __launch_bounds__(BLK / 16 * 64) void bwd_dq_kernel(
+__global__ __launch_bounds__(BLK / 16 * 64, HD <= 64 ? 1 : 2) void bwd_dq_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ o,
     const T *__restrict__ dout, const float *__restrict__ lse, float *__restrict__ dvec, T *__restrict__ dq,
     WorkLists wl, float sl2, float scale) {
@@ -336,8 +338,23 @@ __global__ __launch_bounds__(BLK / 16 * 64) void bwd_dq_kernel(
 }
 
 template <typename T, int BLK, int HD>
-gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream, int stages) {
+gsa_status launch_dq_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream) {
   using S = AttnShape<T, BLK, HD>;
+  const gsa_fwd_args &f = a.f;
+  const int64_t items = f.batch * f.heads * (int64_t)m.n_blocks;
+  const float scale = f.scale > 0.f ? f.scale : 1.0f / sqrtf((float)HD);
+  const WorkLists wl{m.work_row, m.col_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
+                     mask_cap(m.n_blocks)};
+  hipLaunchKernelGGL((bwd_dq_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream,
+                     static_cast<const T *>(f.q), static_cast<const T *>(f.k), static_cast<const T *>(f.v),
+                     static_cast<const T *>(f.o), static_cast<const T *>(a.dout), f.lse, a.workspace,
+                     static_cast<T *>(a.dq), wl, scale * kLog2e, scale);
+  return check_launch("bwd_dq_kernel");
+}
+
+#ifndef GSA_WIDE_TU
+template <typename T, int BLK, int HD>
+gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream, int stages) {
   using SK = AttnShape<T, BLK, HD, dkdv_groups<T, BLK, HD>()>;
   const gsa_fwd_args &f = a.f;
   const int64_t items = f.batch * f.heads * (int64_t)m.n_blocks;
@@ -359,11 +376,12 @@ gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStre
     if (st != GSA_OK) return st;
   }
   if (stages & kBwdDq) {
-    const WorkLists wl{m.work_row, m.col_idx, f.heads, m.n_blocks, m.n_heads[0], m.n_heads[1],
-                       mask_cap(m.n_blocks)};
-    hipLaunchKernelGGL((bwd_dq_kernel<T, BLK, HD>), dim3((unsigned)items), dim3(S::kThreads), 0, stream, q, k, v,
-                       o, dout, f.lse, a.workspace, static_cast<T *>(a.dq), wl, sl2, scale);
-    gsa_status st = check_launch("bwd_dq_kernel");
+    gsa_status st;
+    if constexpr (std::is_same<T, bf16_t>::value && BLK == 128 && HD == 128) {
+      st = launch_dq_wide(a, m, stream);
+    } else {
+      st = launch_dq_instance<T, BLK, HD>(a, m, stream);
+    }
     if (st != GSA_OK) return st;
   }
   if (stages & kBwdDkdv) {
@@ -377,9 +395,15 @@ gsa_status launch_bwd_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStre
   }
   return GSA_OK;
 }
+#endif
 
 }  // namespace
 
+#ifdef GSA_WIDE_TU
+gsa_status launch_dq_wide(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream) {
+  return launch_dq_instance<bf16_t, 128, 128>(a, m, stream);
+}
+#else
 gsa_status launch_attn_bwd(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream, int stages) {
   const gsa_fwd_args &f = a.f;
   if (f.dtype == GSA_F32 && f.block == 16 && f.head_dim == 32)
@@ -391,5 +415,6 @@ gsa_status launch_attn_bwd(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t
   return fail(GSA_ERR_UNSUPPORTED, "no backward kernel for dtype %d, block %d, head_dim %d", f.dtype, f.block,
               f.head_dim);
 }
+#endif
 
 }  // namespace gsa

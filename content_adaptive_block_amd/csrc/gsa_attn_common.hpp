@@ -89,24 +89,38 @@ __device__ __forceinline__ uint32_t dispatch_position(uint32_t b, uint32_t total
   }
 }
 
+// Rows of the K and V pieces that the forward and dQ kernels stream through their LDS
+// ring.  A 128-row block of 128 bf16 features is a 32 KiB tile; streamed as two 64-row
+// pieces, the three ring slots take 48 KiB, so two workgroups share a CU instead of one.
+#ifndef GSA_PIECE_ROWS_128
+#define GSA_PIECE_ROWS_128 64
+#endif
+template <typename T, int BLK, int HD>
+constexpr int kv_piece_rows() {
+  return std::is_same<T, bf16_t>::value && BLK == 128 && HD == 128 ? GSA_PIECE_ROWS_128 : BLK;
+}
+
 // R = 16-row groups owned by each wave (1 or 2); the workgroup has BLK / (16 R) waves.
-template <typename T, int BLK, int HD, int R = 1>
+// KC = rows of a staged tile: the whole block (BLK), or a part of it when the other side
+// streams each block in KC-row pieces.
+template <typename T, int BLK, int HD, int R = 1, int KC = BLK>
 struct AttnShape {
   static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static_assert(kBf16 || std::is_same<T, float>::value, "bf16 or fp32 only");
   static_assert(BLK % (kBf16 ? 32 : 16) == 0 && HD % (kBf16 ? 32 : 16) == 0, "tile shape");
+  static_assert(KC % (kBf16 ? 32 : 16) == 0 && BLK % KC == 0, "staged rows");
   static_assert(R >= 1 && BLK % (16 * R) == 0, "row groups per wave");
   static constexpr int kWaves = BLK / (16 * R);
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kKB = BLK / 16;                 // 16-row tiles of a staged block
+  static constexpr int kKB = KC / 16;                  // 16-row tiles of a staged tile
   static constexpr int kDB = HD / 16;                  // 16-wide feature tiles
   static constexpr int kKS = kBf16 ? HD / 32 : HD / 4; // MFMA K-steps over the features
   static constexpr int kVec = 16 / sizeof(T);          // elements per 16-byte chunk
   static constexpr int kRowBytes = HD * sizeof(T);
   static constexpr int kChunks = kRowBytes / 16;       // chunks per row
   static_assert(kChunks == 8 || kChunks == 16, "rows of 128 or 256 bytes");
-  static constexpr int kTileBytes = BLK * kRowBytes;
-  static constexpr int kTileChunks = BLK * kChunks;
+  static constexpr int kTileBytes = KC * kRowBytes;
+  static constexpr int kTileChunks = KC * kChunks;
   static_assert(kTileChunks % kThreads == 0, "staging must divide evenly");
   static constexpr int kChunksPerThread = kTileChunks / kThreads;
 
@@ -134,7 +148,7 @@ struct AttnShape {
     }
   }
 
-  // Asynchronous copy of a BLK x HD tile into LDS in the swizzled layout: every copy
+  // Asynchronous copy of a KC x HD tile into LDS in the swizzled layout: every copy
   // instruction fills 64 consecutive 16-byte LDS slots, so each lane fetches the global
   // chunk whose swizzled home is its slot.  kTileCopies instructions per thread.
   static constexpr int kTileCopies = kChunksPerThread;
@@ -328,46 +342,57 @@ __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
 // ---------------------------------------------------------------------------------------
 // Three-slot pipeline for items whose two streamed tiles (K_j and V_j) are used one after
 // the other: 3 tiles of LDS instead of 4, which lets 5 rather than 4 workgroups share a
-// CU (gfx950 fits five 24 KiB workgroups but only four 32 KiB ones).  Per step e:
-//   wait for K_e and V_e, barrier (everyone left step e - 1, so the spare slot is free);
-//   copy K_{e+1} into the spare slot; compute_a (reads K_e, and V_e if it wants);
-//   barrier (everyone is done with the slot the policy frees: K_e when kFreeK, else V_e);
-//   copy V_{e+1} into it; compute_b.
-// The policy supplies operands/begin/finish as for run_item, plus
-//   copy_k(item, j, slot), copy_v(item, j, slot), compute_a(item, e, k_slot, v_slot),
-//   compute_b(item, e, k_slot, v_slot) and the constant kFreeK.
+// CU (gfx950 fits five 24 KiB workgroups but only four 32 KiB ones).  Each list entry is
+// streamed as P::kSub pieces of BLK / kSub rows (one piece unless the tiles are large);
+// per piece:
+//   wait for K and V, barrier (everyone left the previous piece, so the spare slot is
+//   free); copy the next piece's K into the spare slot; compute_a (reads K, and V if it
+//   wants); barrier (everyone is done with the slot the policy frees: K when kFreeK, else
+//   V); copy the next piece's V into it; compute_b.
+// The policy supplies operands/begin/finish as for run_item, plus the constants kSub and
+// kFreeK, copy_k(item, j, piece, slot), copy_v(item, j, piece, slot),
+// compute_a(item, e, piece, k_slot, v_slot) and compute_b(item, e, piece, k_slot, v_slot).
 // ---------------------------------------------------------------------------------------
 template <class P>
 __device__ __forceinline__ void run_item_ring(P &pol, const WorkItem &it) {
+  constexpr int kSub = P::kSub;
   const int lane = threadIdx.x & (kWave - 1);
   int chunk = it.beg + 1 + lane < it.end ? it.list[it.beg + 1 + lane] : 0;
   pol.operands(it);
   int ks = 0, vs = 1, spare = 2;
-  pol.copy_k(it, it.first, ks);
-  pol.copy_v(it, it.first, vs);
+  pol.copy_k(it, it.first, 0, ks);
+  pol.copy_v(it, it.first, 0, vs);
   pol.begin(it);
+  int j = it.first;
   for (int e = it.beg; e < it.end; ++e) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    wg_barrier();
     const int nx_pos = e - it.beg;   // entry e + 1 sits at this position of the chunk run
-    const bool more = e + 1 < it.end;
-    int j_next = 0;
-    if (more) {
-      if (nx_pos > 0 && (nx_pos & (kWave - 1)) == 0)
-        chunk = e + 1 + lane < it.end ? it.list[e + 1 + lane] : 0;
-      j_next = __builtin_amdgcn_readlane(chunk, nx_pos & (kWave - 1));
-      pol.copy_k(it, j_next, spare);
+#pragma unroll
+    for (int h = 0; h < kSub; ++h) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wg_barrier();
+      const bool last_piece = h + 1 == kSub;
+      const bool more = !last_piece || e + 1 < it.end;
+      int j_next = j;
+      if (last_piece && e + 1 < it.end) {
+        if (nx_pos > 0 && (nx_pos & (kWave - 1)) == 0)
+          chunk = e + 1 + lane < it.end ? it.list[e + 1 + lane] : 0;
+        j_next = __builtin_amdgcn_readlane(chunk, nx_pos & (kWave - 1));
+      }
+      const int h_next = last_piece ? 0 : h + 1;
+      if (more) pol.copy_k(it, j_next, h_next, spare);
+      pol.compute_a(it, e, h, ks, vs);
+      wg_barrier();
+      const int freed = P::kFreeK ? ks : vs;
+      if (more) pol.copy_v(it, j_next, h_next, freed);
+      pol.compute_b(it, e, h, ks, vs);
+      // The next piece's K sits in the spare slot and its V in the freed one; the other
+      // is spare.
+      const int next_spare = P::kFreeK ? vs : ks;
+      ks = spare;
+      vs = freed;
+      spare = next_spare;
+      j = j_next;
     }
-    pol.compute_a(it, e, ks, vs);
-    wg_barrier();
-    const int freed = P::kFreeK ? ks : vs;
-    if (more) pol.copy_v(it, j_next, freed);
-    pol.compute_b(it, e, ks, vs);
-    // K_{e+1} sits in the spare slot and V_{e+1} in the freed one; the other is spare.
-    const int next_spare = P::kFreeK ? vs : ks;
-    ks = spare;
-    vs = freed;
-    spare = next_spare;
   }
   pol.finish(it);
 }

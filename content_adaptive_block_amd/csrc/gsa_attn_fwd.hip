@@ -51,8 +51,10 @@ constexpr int fwd_groups() {
 
 template <typename T, int BLK, int HD, int R>
 struct FwdPolicy {
-  using S = AttnShape<T, BLK, HD, R>;
+  static constexpr int KC = kv_piece_rows<T, BLK, HD>();
+  using S = AttnShape<T, BLK, HD, R, KC>;
   using Item = WorkItem;
+  static constexpr int kSub = BLK / KC;   // pieces per kv-block
   static constexpr int kLdsBytes = 3 * S::kTileBytes;
 
   const T *q, *k, *v;
@@ -82,15 +84,15 @@ struct FwdPolicy {
     }
   }
   static constexpr bool kFreeK = true;   // K_j is done once the scores are
-  __device__ void copy_k(const Item &it, int j, int slot) {
-    S::copy_tile(lds + slot * S::kTileBytes, k + (it.sh * seq + (int64_t)j * BLK) * HD, tid);
+  __device__ void copy_k(const Item &it, int j, int piece, int slot) {
+    S::copy_tile(lds + slot * S::kTileBytes, k + (it.sh * seq + (int64_t)j * BLK + piece * KC) * HD, tid);
   }
-  __device__ void copy_v(const Item &it, int j, int slot) {
-    S::copy_tile(lds + slot * S::kTileBytes, v + (it.sh * seq + (int64_t)j * BLK) * HD, tid);
+  __device__ void copy_v(const Item &it, int j, int piece, int slot) {
+    S::copy_tile(lds + slot * S::kTileBytes, v + (it.sh * seq + (int64_t)j * BLK + piece * KC) * HD, tid);
   }
-  // S^T tiles: lane holds keys kb*16 + 4g + rr of query q0 + 16 r.
+  // S^T tiles: lane holds keys piece*KC + kb*16 + 4g + rr of query q0 + 16 r.
   f32x4 st[R][S::kKB];
-  __device__ void compute_a(const Item &it, int e, int k_slot, int) {
+  __device__ void compute_a(const Item &it, int e, int piece, int k_slot, int) {
     const unsigned char *lk = lds + k_slot * S::kTileBytes;
 #pragma unroll
     for (int kb = 0; kb < S::kKB; ++kb) {
@@ -106,7 +108,7 @@ struct FwdPolicy {
         for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
-            if (kb * 16 + 4 * g + rr > q0 + 16 * r) st[r][kb][rr] = kMaskedScore;
+            if (piece * KC + kb * 16 + 4 * g + rr > q0 + 16 * r) st[r][kb][rr] = kMaskedScore;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -133,7 +135,7 @@ struct FwdPolicy {
         }
     }
   }
-  __device__ void compute_b(const Item &, int, int, int v_slot) {
+  __device__ void compute_b(const Item &, int, int, int, int v_slot) {
     const unsigned char *lv = lds + v_slot * S::kTileBytes;
 #pragma unroll
     for (int part = 0; part < S::kParts; ++part)
@@ -158,7 +160,7 @@ template <typename T, int BLK, int HD>
 // with two row groups per wave): the three-tile ring lets five or six workgroups share a
 // CU's LDS, and registers must not be the tighter limit.
 __global__ __launch_bounds__((BLK / (16 * fwd_groups<T, BLK, HD>()) * 64),
-                             (HD <= 64 ? (fwd_groups<T, BLK, HD>() == 1 ? 5 : 3) : 1)) void attn_fwd_kernel(
+                             (HD <= 64 ? (fwd_groups<T, BLK, HD>() == 1 ? 5 : 3) : 2)) void attn_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
     float *__restrict__ lse, WorkLists wl, float sl2) {
   constexpr int R = fwd_groups<T, BLK, HD>();
@@ -198,6 +200,11 @@ gsa_status launch_fwd_instance(const gsa_fwd_args &a, const gsa_mask &m, hipStre
 
 }  // namespace
 
+#ifdef GSA_WIDE_TU
+gsa_status launch_attn_fwd_wide(const gsa_fwd_args &a, const gsa_mask &m, hipStream_t stream) {
+  return launch_fwd_instance<bf16_t, 128, 128>(a, m, stream);
+}
+#else
 bool attn_instance_built(int32_t dtype, int32_t block, int32_t head_dim) {
   if (dtype == GSA_F32) return block == 16 && head_dim == 32;
   if (dtype == GSA_BF16) return (block == 64 && head_dim == 64) || (block == 128 && head_dim == 128);
@@ -209,10 +216,10 @@ gsa_status launch_attn_fwd(const gsa_fwd_args &a, const gsa_mask &m, hipStream_t
     return launch_fwd_instance<float, 16, 32>(a, m, stream);
   if (a.dtype == GSA_BF16 && a.block == 64 && a.head_dim == 64)
     return launch_fwd_instance<bf16_t, 64, 64>(a, m, stream);
-  if (a.dtype == GSA_BF16 && a.block == 128 && a.head_dim == 128)
-    return launch_fwd_instance<bf16_t, 128, 128>(a, m, stream);
+  if (a.dtype == GSA_BF16 && a.block == 128 && a.head_dim == 128) return launch_attn_fwd_wide(a, m, stream);
   return fail(GSA_ERR_UNSUPPORTED, "no forward kernel for dtype %d, block %d, head_dim %d", a.dtype,
               a.block, a.head_dim);
 }
+#endif
 
 }  // namespace gsa

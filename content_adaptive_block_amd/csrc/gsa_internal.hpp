@@ -27,6 +27,11 @@ gsa_status launch_attn_fwd(const gsa_fwd_args &a, const gsa_mask &m, hipStream_t
 // enqueued in the order D alone, dQ, dK/dV.
 enum : int { kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = kBwdDq | kBwdDkdv };
 gsa_status launch_attn_bwd(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream, int stages);
+// The 128 x 128 bf16 forward and dQ, built in a translation unit of their own with the
+// occupancy-first instruction scheduler (it keeps them within 128 VGPRs, so two
+// workgroups share a CU).
+gsa_status launch_attn_fwd_wide(const gsa_fwd_args &a, const gsa_mask &m, hipStream_t stream);
+gsa_status launch_dq_wide(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream);
 
 // Whether a (dtype, block, head_dim) instance is compiled in.
 bool attn_instance_built(int32_t dtype, int32_t block, int32_t head_dim);
