@@ -69,15 +69,30 @@ constexpr int dkdv_groups() {
   return std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0 ? GSA_DKDV_GROUPS : 1;
 }
 
+// Query rows per streamed piece of dK/dV (GSA_DKDV_PIECE at b = 64, d = 64, bf16).  With
+// 32-row pieces a workgroup's two stages take 16.5 KiB instead of 33, and the kernel is
+// asked for three waves per SIMD (<= 168 VGPRs), so six 2-wave workgroups share a CU
+// instead of four: 3-5% faster at 8 x 8 KiB; the same pieces at two waves per SIMD were
+// 3% slower than whole blocks.
+#ifndef GSA_DKDV_PIECE
+#define GSA_DKDV_PIECE 32
+#endif
+template <typename T, int BLK, int HD>
+constexpr int dkdv_piece_rows() {
+  return std::is_same<T, bf16_t>::value && BLK == 64 && HD == 64 ? GSA_DKDV_PIECE : BLK;
+}
+
 // dK, dV of one (sample, head, kv-block j): walk the query blocks i of column j.  Each
 // wave owns R groups of 16 keys of block j.
 template <typename T, int BLK, int HD, int R>
 struct DkdvPolicy {
-  using S = AttnShape<T, BLK, HD, R>;
+  static constexpr int KQ = dkdv_piece_rows<T, BLK, HD>();
+  using S = AttnShape<T, BLK, HD, R, KQ>;
   using Item = WorkItem;
-  // A stage holds Q_i, dO_i, then LSE_i and D_i (BLK floats each).
-  static constexpr int kStageBytes = 2 * S::kTileBytes + 2 * BLK * 4;
-  static constexpr int kVecLanes = BLK / S::kWaves;   // floats of LSE_i (and D_i) per wave
+  static constexpr int kSub = BLK / KQ;   // pieces per query block
+  // A stage holds KQ rows of Q_i and of dO_i, then KQ floats each of LSE_i and D_i.
+  static constexpr int kStageBytes = 2 * S::kTileBytes + 2 * KQ * 4;
+  static constexpr int kVecLanes = KQ / S::kWaves;   // floats of LSE_i (and D_i) per wave
   static_assert(kVecLanes <= 64, "vector slice per wave");
 
   const T *q, *k, *v, *dout;
@@ -118,8 +133,8 @@ struct DkdvPolicy {
         dv_acc[kg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
   }
-  __device__ void copy(const Item &it, int i, int stage) {
-    const int64_t row0 = it.sh * seq + (int64_t)i * BLK;
+  __device__ void copy(const Item &it, int i, int piece, int stage) {
+    const int64_t row0 = it.sh * seq + (int64_t)i * BLK + piece * KQ;
     unsigned char *dst = lds + stage * kStageBytes;
     S::copy_tile(dst, q + row0 * HD, tid);
     S::copy_tile(dst + S::kTileBytes, dout + row0 * HD, tid);
@@ -127,17 +142,17 @@ struct DkdvPolicy {
     if (lane < kVecLanes) {
       const int x = wave * kVecLanes + lane;
       copy4_to_lds(lse + row0 + x, dst + 2 * S::kTileBytes + wave * kVecLanes * 4);
-      copy4_to_lds(dvec + row0 + x, dst + 2 * S::kTileBytes + BLK * 4 + wave * kVecLanes * 4);
+      copy4_to_lds(dvec + row0 + x, dst + 2 * S::kTileBytes + KQ * 4 + wave * kVecLanes * 4);
     }
   }
-  __device__ void compute(const Item &it, int e, int stage) {
+  __device__ void compute(const Item &it, int e, int piece, int stage) {
     const unsigned char *lq = lds + stage * kStageBytes;
     const unsigned char *ldo = lq + S::kTileBytes;
     const float *ll = reinterpret_cast<const float *>(lq + 2 * S::kTileBytes);
-    const float *ld = ll + BLK;
+    const float *ld = ll + KQ;
     const bool diag = e == it.beg;   // column j starts with its own block i = j
     // P[q][key] and dS[q][key], one part of 16*kPartTiles queries at a time;
-    // lane: key c of each group, queries qb*16 + 4g + r.
+    // lane: key c of each group, queries piece*KQ + qb*16 + 4g + r.
 #pragma unroll
     for (int part = 0; part < S::kParts; ++part) {
       f32x4 p[R][S::kPartTiles], ds[R][S::kPartTiles];
@@ -162,7 +177,7 @@ struct DkdvPolicy {
           for (int kg = 0; kg < R; ++kg)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (key0 + 16 * kg > qb * 16 + 4 * g + r) {
+              if (key0 + 16 * kg > piece * KQ + qb * 16 + 4 * g + r) {
                 p[kg][t][r] = 0.f;
                 ds[kg][t][r] = 0.f;
               }
@@ -189,7 +204,8 @@ struct DkdvPolicy {
 };
 
 template <typename T, int BLK, int HD>
-__global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64)) void bwd_dkdv_kernel(
+__global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64),
+                             (dkdv_piece_rows<T, BLK, HD>() < BLK ? 3 : 1)) void bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ dvec, T *__restrict__ dk, T *__restrict__ dv,
     WorkLists wl, float sl2, float scale) {

@@ -301,16 +301,16 @@ struct AttnShape {
 
 // ---------------------------------------------------------------------------------------
 // Per-item pipeline shared by the attention kernels.  A workgroup runs one work item,
-// which walks one list (a CSR row or a CSC column); each list entry's tiles arrive in
-// one of two LDS stages by asynchronous copies issued one entry ahead.  The policy P
-// supplies:
-//   operands(item)                 load the item's register operands (before the loop)
-//   begin(item)                    clear the accumulators
-//   copy(item, entry, stage)       issue the copies of one list entry into `stage`
-//   compute(item, e, stage)        one list entry (e indexes item.list)
-//   finish(item)                   write the item's outputs
+// which walks one list (a CSR row or a CSC column); each list entry's block arrives as
+// P::kSub pieces of BLK / kSub rows, each piece in one of two LDS stages by asynchronous
+// copies issued one piece ahead.  The policy P supplies kSub and:
+//   operands(item)                   load the item's register operands (before the loop)
+//   begin(item)                      clear the accumulators
+//   copy(item, block, piece, stage)  issue the copies of one piece into `stage`
+//   compute(item, e, piece, stage)   one piece of list entry e (e indexes item.list)
+//   finish(item)                     write the item's outputs
 // A step waits for its own copies, synchronises -- after which every wave has finished
-// the previous step, so the other stage is free -- issues the next entry's copies and
+// the previous step, so the other stage is free -- issues the next piece's copies and
 // computes.
 // ---------------------------------------------------------------------------------------
 template <class P>
@@ -319,21 +319,28 @@ __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
   // per lane), read with readlane: no step waits on memory for its next kv index.
   const int lane = threadIdx.x & (kWave - 1);
   int chunk = it.beg + 1 + lane < it.end ? it.list[it.beg + 1 + lane] : 0;
+  constexpr int kSub = P::kSub;
   pol.operands(it);
-  pol.copy(it, it.first, 0);
+  pol.copy(it, it.first, 0, 0);
   pol.begin(it);
-  int stage = 0;
+  int stage = 0, j = it.first;
   for (int e = it.beg; e < it.end; ++e) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    wg_barrier();
     const int nx = e + 1 - (it.beg + 1);   // position of entry e + 1 after the first
-    if (e + 1 < it.end) {
-      if (nx > 0 && (nx & (kWave - 1)) == 0)
-        chunk = e + 1 + lane < it.end ? it.list[e + 1 + lane] : 0;
-      pol.copy(it, __builtin_amdgcn_readlane(chunk, nx & (kWave - 1)), stage ^ 1);
+#pragma unroll
+    for (int h = 0; h < kSub; ++h) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wg_barrier();
+      if (h + 1 < kSub) {
+        pol.copy(it, j, h + 1, stage ^ 1);
+      } else if (e + 1 < it.end) {
+        if (nx > 0 && (nx & (kWave - 1)) == 0)
+          chunk = e + 1 + lane < it.end ? it.list[e + 1 + lane] : 0;
+        j = __builtin_amdgcn_readlane(chunk, nx & (kWave - 1));
+        pol.copy(it, j, 0, stage ^ 1);
+      }
+      pol.compute(it, e, h, stage);
+      stage ^= 1;
     }
-    pol.compute(it, e, stage);
-    stage ^= 1;
   }
   pol.finish(it);
 }
