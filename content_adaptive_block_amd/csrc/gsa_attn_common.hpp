@@ -348,8 +348,8 @@ __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
 
 // ---------------------------------------------------------------------------------------
 // Three-slot pipeline for items whose two streamed tiles (K_j and V_j) are used one after
-// the other: 3 tiles of LDS instead of 4, which lets 5 rather than 4 workgroups share a
-// CU (gfx950 fits five 24 KiB workgroups but only four 32 KiB ones).  Each list entry is
+// the other: 3 tiles of LDS instead of 4, which lets 6 rather than 4 workgroups share a
+// CU (gfx950 fits six 24 KiB workgroups but only four 32 KiB ones).  Each list entry is
 // streamed as P::kSub pieces of BLK / kSub rows (one piece unless the tiles are large);
 // per piece:
 //   wait for K and V, barrier (everyone left the previous piece, so the spare slot is
