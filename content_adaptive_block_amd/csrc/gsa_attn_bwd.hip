@@ -13,11 +13,13 @@
 //             (query blocks i that keep j); each wave keeps 16 or 32 keys of K_j, V_j in
 //             registers and accumulates dK^T, dV^T tiles in fp32 while Q_i, dO_i, LSE_i
 //             and D_i stream through two LDS stages by asynchronous global -> LDS copies
-//             one block ahead; Q_i^T and dO_i^T come from transposing LDS reads.
+//             one piece ahead (32-row pieces at b = 64, whole blocks otherwise); Q_i^T
+//             and dO_i^T come from transposing LDS reads.
 //   bwd_dq    one workgroup per (sample, head, query block i), walking the CSR row of i;
 //             each wave keeps 16 query rows of Q_i and dO_i in registers and accumulates
-//             dQ^T while K_j and V_j stream through a ring of three LDS tiles (V_j's
-//             tile takes V_{j+1} as soon as dS is formed; K_j^T by transposing reads).
+//             dQ^T while K_j and V_j stream through a ring of three LDS slots (V's slot
+//             takes the next V as soon as dS is formed; K^T by transposing reads); at
+//             b = 128, d = 128 the blocks stream as 64-row pieces.
 //             It also forms D of its rows from O and dO and writes it for dK/dV, so the
 //             full backward runs dQ, then dK/dV, with no separate pass for D.
 #include <type_traits>

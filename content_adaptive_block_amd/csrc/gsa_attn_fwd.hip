@@ -16,7 +16,8 @@
 //     two products.
 //   * K_j and V_j stream row-major (swizzled) into a ring of three LDS tiles by
 //     asynchronous global -> LDS copies: K_{j+1} lands in the spare tile while block j
-//     is computed, V_{j+1} in K_j's tile once the scores of block j are done.  O^T =
+//     is computed, V_{j+1} in K_j's tile once the scores of block j are done (at
+//     b = 128, d = 128 in 64-row pieces, so that two workgroups fit a CU).  O^T =
 //     V^T P^T reads V^T with transposing LDS loads and takes P straight from the S^T
 //     accumulator (rounded to bf16 in the bf16 instance).
 //   * Scores are scaled by scale * log2(e) so every exponential is one exp2.  The
