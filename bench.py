@@ -15,7 +15,9 @@ Prints ONE JSON line.  ``value`` is effective TFLOP/s on kept blocks: algorithmi
 FLOPs (4 b^2 d per kept tile forward, 10 b^2 d backward, diagonal tiles counted whole)
 divided by the step time.  ``roofline`` rates the kernel that takes the most time per
 step against its binding MI355X roof, from HIP events around each kernel on its stream;
-``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload and
+compares the timed step's outputs on that sample with it (``cpu_baseline.parity``);
+``env`` names the GPU, HIP, torch and zlib versions and the seeds.
 """
 from __future__ import annotations
 
@@ -152,8 +154,12 @@ def record_traffic(args, fetch_csv: str, write_csv: str):
     print(f"\nscale: FETCH x {scale_f:.4f}, WRITE x {scale_w:.4f} (copy of {args.copy_mib} MiB)")
 
 
-def cpu_baseline(wl, x_bytes, tensors, masks_np, budget_s: float):
-    """The fp64 oracle on whole heads of sample 0 until ``budget_s`` seconds are spent."""
+def cpu_baseline(wl, x_bytes, tensors, device_out, budget_s: float):
+    """The fp64 oracle on whole heads of sample 0 until ``budget_s`` seconds are spent.
+
+    ``device_out`` holds the timed step's outputs for sample 0 (O, LSE and, for backward
+    workloads, dQ, dK, dV); each head the oracle finishes is compared with them, and the
+    largest absolute error per tensor is reported beside the largest reference value."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -169,26 +175,42 @@ def cpu_baseline(wl, x_bytes, tensors, masks_np, budget_s: float):
     f64 = lambda z: z.float().numpy().astype(np.float64)
     done, flops, t_attn = 0, 0.0, 0.0
     tile = wl.block * wl.block * wl.head_dim
+    names = ("o", "lse", "dq", "dk", "dv") if wl.backward else ("o", "lse")
+    err = {nm: 0.0 for nm in names}
+    ref_max = {nm: 0.0 for nm in names}
     for h in range(wl.heads):
-        q, k, v, do = (f64(tensors[nm][0:1, h:h + 1]) for nm in ("q", "k", "v", "do"))
+        q, k, v = (f64(tensors[nm][0:1, h:h + 1]) for nm in ("q", "k", "v"))
         nh = [0, 0, 0]
         nh[classes[h]] = 1
         sub = np.zeros((1, 3) + bm.shape[2:], dtype=bool)
         sub[0, classes[h]] = bm[0, classes[h]]
         t1 = time.perf_counter()
-        oracle.attn_fwd(q, k, v, sub, tuple(nh), wl.block)
+        refs = list(oracle.attn_fwd(q, k, v, sub, tuple(nh), wl.block))
         if wl.backward:
-            oracle.attn_bwd(q, k, v, do, sub, tuple(nh), wl.block)
+            do = f64(tensors["do"][0:1, h:h + 1])
+            refs += list(oracle.attn_bwd(q, k, v, do, sub, tuple(nh), wl.block))
         t_attn += time.perf_counter() - t1
+        if device_out is not None:
+            for nm, ref in zip(names, refs):
+                got = device_out[nm][h].double().numpy()
+                err[nm] = max(err[nm], float(np.max(np.abs(got - ref[0, 0]))))
+                ref_max[nm] = max(ref_max[nm], float(np.max(np.abs(ref))))
         flops += (14 if wl.backward else 4) * tile * int(bm[0, classes[h]].sum())
         done += 1
         if t_attn + t_mask >= budget_s:
             break
     secs = t_attn + t_mask
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"sample 0 of {wl.batch}, {done} of {wl.heads} heads, full {wl.seq_len}-byte context; "
-                      f"zlib+mask {t_mask:.2f} s, attention fwd{'+bwd' if wl.backward else ''} {t_attn:.2f} s",
-            "seconds": secs}
+    rec = {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"sample 0 of {wl.batch}, {done} of {wl.heads} heads, full {wl.seq_len}-byte context; "
+                     f"zlib+mask {t_mask:.2f} s, attention fwd{'+bwd' if wl.backward else ''} {t_attn:.2f} s",
+           "seconds": secs}
+    if device_out is not None:
+        # the tolerances of the parity tests: absolute, on values of order one
+        tol = {nm: (1e-5 if wl.dtype == "f32" else (1e-3 if nm == "lse" else 2e-2)) for nm in names}
+        rec["parity"] = {"heads": done, "tensors": {nm: {"max_abs_err": err[nm], "max_abs_ref": ref_max[nm],
+                                                          "tol": tol[nm]} for nm in names},
+                         "within_tol": all(err[nm] <= tol[nm] for nm in names)}
+    return rec
 
 
 class DevicePath:
@@ -357,6 +379,11 @@ def main():
     path = DevicePath(torch, gsa, wl, c, t, dev)
     ms_step, kern_ms = path.time(args.steps, args.warmup, args.settle_ms)
     mask = path.mask
+    # The timed steps' outputs for sample 0, for the oracle comparison in cpu_baseline.
+    device_out = None
+    if args.cpu_budget > 0:
+        outs = (path.o, path.lse) + (path.grads if wl.backward else ())
+        device_out = {nm: x_[0].float().cpu() for nm, x_ in zip(("o", "lse", "dq", "dk", "dv"), outs)}
     # The hand-over of c from pinned host memory (4 bytes per block over PCIe), timed on
     # its own: the step starts from c resident in HBM.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -538,9 +565,13 @@ def main():
         "host_prepare_ms": {"all_cores": round(prep_ms, 3), "one_thread": round(prep1_ms, 3)},
         "kernels": kernels, "roofline": roof, "cold": cold, "dense_causal": dense,
         "host_pipeline": pipeline, "layer": layer, "bigbird": bigbird,
+        "n_edges": n_edges.tolist(),
+        "env": {"gpu": torch.cuda.get_device_name(dev), "hip": torch.version.hip, "torch": torch.__version__,
+                "zlib": gsa.zlib_version(), "host_cpus": os.cpu_count(),
+                "seeds": f"numpy default_rng([{wl.seed_id}, stream]); streams: bytes 0, q 1, k 2, v 3, do 4"},
     }
     if args.cpu_budget > 0:
-        rec["cpu_baseline"] = cpu_baseline(wl, x, host_t, None, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, host_t, device_out, args.cpu_budget)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

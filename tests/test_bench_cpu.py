@@ -88,3 +88,25 @@ def test_traffic_records(name):
     assert compulsory <= rec["bytes_per_launch"] < 2 * compulsory
     current = rec["source_hash"] == bench.kernel_source_hash(name)
     assert bench.load_traffic(name, wl) == (float(rec["bytes_per_launch"]) if current else None)
+
+
+def test_cpu_baseline_reports_parity_against_the_device_outputs():
+    # device outputs equal to the oracle's give zero error; a perturbed O exceeds the fp32
+    # tolerance and is reported as such
+    import torch
+    wl = synth.WORKLOADS[1]                        # 1 x 256 B, b 16, 4 heads, d 32, fp32, fwd
+    x = synth.gen_bytes(wl)
+    t = synth.gen_tensors(wl, ("q", "k", "v"))
+    c = oracle.compressed_lengths(x[:1], wl.block)
+    flags, _ = oracle.literal_flags(c, wl.block)
+    bm = oracle.block_masks(flags, wl.window)
+    f64 = lambda z: z.double().numpy()
+    o, lse = oracle.attn_fwd(f64(t["q"][:1]), f64(t["k"][:1]), f64(t["v"][:1]), bm, wl.n_heads, wl.block)
+    dev = {"o": torch.from_numpy(o[0]).float(), "lse": torch.from_numpy(lse[0]).float()}
+    rec = bench.cpu_baseline(wl, x, t, dev, budget_s=60.0)
+    par = rec["parity"]
+    assert par["heads"] == wl.heads and par["within_tol"]
+    assert par["tensors"]["o"]["max_abs_err"] < 1e-6 and par["tensors"]["o"]["max_abs_ref"] > 0.1
+    dev["o"] = dev["o"] + 1e-3
+    par = bench.cpu_baseline(wl, x, t, dev, budget_s=60.0)["parity"]
+    assert not par["within_tol"] and abs(par["tensors"]["o"]["max_abs_err"] - 1e-3) < 1e-6
