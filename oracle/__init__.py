@@ -8,4 +8,4 @@ from .gsa_oracle import (LOCAL, LITERAL, HYBRID, CLASS_NAMES, zlib_runtime_versi
                          gzip_member, gzip_length, compressed_lengths, literal_flags,
                          block_mask, block_masks, default_head_counts, head_classes,
                          to_csr, to_csc, token_mask, attn_fwd, attn_fwd_rows, attn_bwd,
-                         attn_bwd_qblock, attn_bwd_kblock, edge_counts, prepare_and_mask)
+                         attn_bwd_qblock, attn_bwd_kblock, kept_keys)

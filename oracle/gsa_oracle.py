@@ -219,16 +219,16 @@ def to_csc(mask: np.ndarray):
     return to_csr(np.ascontiguousarray(mask.T))
 
 
-def token_mask(bmask: np.ndarray, block: int, rows=None) -> np.ndarray:
-    """A[t, u] = M[t // b, u // b] and u <= t over all keys u in [0, T).
+def token_mask(bmask: np.ndarray, block: int, rows=None, keys=None) -> np.ndarray:
+    """A[t, u] = M[t // b, u // b] and u <= t.
 
     Causality at token level as in [note] 核心公式 ("intersected with the causal mask").
-    ``rows`` selects query positions (default all).
+    ``rows`` selects query positions and ``keys`` key positions (default all of [0, T)).
     """
     n = bmask.shape[0]
     seq_len = n * block
     t = np.arange(seq_len) if rows is None else np.asarray(rows)
-    u = np.arange(seq_len)
+    u = np.arange(seq_len) if keys is None else np.asarray(keys)
     return bmask[t[:, None] // block, u[None, :] // block] & (u[None, :] <= t[:, None])
 
 
@@ -236,22 +236,32 @@ def _scale(head_dim: int, scale):
     return 1.0 / np.sqrt(head_dim) if not scale else float(scale)
 
 
-def _rows_forward(q, k, v, bmask, block, scale, rows):
+def kept_keys(bmask: np.ndarray, block: int, i: int) -> np.ndarray:
+    """Token positions of the key blocks that query block i keeps (row i of ``bmask``,
+    causal part), ascending."""
+    js = np.nonzero(bmask[i, :i + 1])[0]
+    return (js[:, None] * block + np.arange(block)[None, :]).ravel()
+
+
+def _rows_forward(q, k, v, bmask, block, scale, rows, keys=None):
     """Dense masked softmax attention for the query positions ``rows`` of one head.
 
-    Scores over the causal prefix [0, max(rows)+1), masked entries set to -inf,
-    max-subtracted softmax, O = P V, LSE = log sum exp of the masked scores.
+    Scores over the key positions ``keys`` (default: the causal prefix
+    [0, max(rows)+1)), masked entries set to -inf, max-subtracted softmax, O = P V,
+    LSE = log sum exp of the masked scores.  Any key outside ``keys`` must be masked
+    for every row; it would carry weight exactly zero, so leaving it out changes nothing.
     """
     rows = np.asarray(rows)
-    prefix = int(rows.max()) + 1
-    a = token_mask(bmask, block, rows)[:, :prefix]
-    s = scale * (q[rows] @ k[:prefix].T)
+    if keys is None:
+        keys = np.arange(int(rows.max()) + 1)
+    a = token_mask(bmask, block, rows, keys)
+    s = scale * (q[rows] @ k[keys].T)
     s = np.where(a, s, -np.inf)
     m = s.max(axis=1)
     p = np.exp(s - m[:, None])
     l = p.sum(axis=1)
     p = p / l[:, None]
-    o = p @ v[:prefix]
+    o = p @ v[keys]
     lse = m + np.log(l)
     return o, lse, p, a
 
@@ -340,30 +350,30 @@ def attn_bwd_kblock(q, k, v, do, bmask, block: int, j: int, scale=None):
     """dK, dV rows of key block j of ONE head, summed over every query block that keeps j.
 
     Query blocks that do not keep block j contribute exact zeros to it, so only the
-    column list of j is visited.  For sampled checks at full size.
+    column list of j is visited.  Each such query block i takes its softmax over the keys
+    of the blocks its row keeps (every other key is masked: weight exactly zero under
+    [note] 核心公式 second display), and only block j's columns of the backward are
+    formed: with P_i the kept softmax of i's rows, O_i = P_i V, D_i = rowsum(dO_i * O_i)
+    and P_ij the columns of P_i that belong to block j,
+      dV_j += P_ij^T dO_i,   dS_ij = P_ij * (dO_i V_j^T - D_i),   dK_j += scale dS_ij^T Q_i.
+    For sampled checks at full size.
     """
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     sc = _scale(q.shape[1], scale)
     n = bmask.shape[0]
-    cols = slice(j * block, (j + 1) * block)
+    cols = np.arange(j * block, (j + 1) * block)
     dk = np.zeros((block, q.shape[1]))
     dv = np.zeros((block, q.shape[1]))
     for i in range(j, n):
         if not bmask[i, j]:
             continue
-        _, g_k, g_v, _ = _qblock_backward(q, k, v, do, bmask, block, sc, i)
-        dk += g_k[cols]
-        dv += g_v[cols]
+        rows = np.arange(i * block, (i + 1) * block)
+        keys = kept_keys(bmask, block, i)
+        o, _, p, _ = _rows_forward(q, k, v, bmask, block, sc, rows, keys)
+        dov = do[rows]
+        dd = (dov * o).sum(axis=1)
+        p_j = p[:, np.searchsorted(keys, cols)]
+        dv += p_j.T @ dov
+        ds = p_j * (dov @ v[cols].T - dd[:, None])
+        dk += sc * (ds.T @ q[rows])
     return dk, dv
-
-
-def edge_counts(bmasks) -> np.ndarray:
-    """Kept block pairs per (sample, class): int64 [B, 3]."""
-    return np.asarray(bmasks).sum(axis=(2, 3)).astype(np.int64)
-
-
-def prepare_and_mask(data, block: int, window: int):
-    """Bytes -> (c, flags, L, block masks), the whole integer half of the path."""
-    c = compressed_lengths(data, block)
-    flags, n_lit = literal_flags(c, block)
-    return c, flags, n_lit, block_masks(flags, window)

@@ -180,3 +180,31 @@ def test_backward_invariants():
     _, _, dv1 = oracle.attn_bwd(q, k, v, np.ones_like(do), bm, (1, 1, 1), b)
     np.testing.assert_allclose(dv1[..., 0].sum(axis=2), n * b, atol=1e-10)
     assert np.allclose(dv1[..., 0:1], dv1)
+
+
+def test_kept_keys_is_the_union_of_visible_positions():
+    # brute force: position u belongs to row i's kept keys iff some query of block i may
+    # see it, i.e. its block is kept by row i and lies at or before i
+    b, n = 3, 7
+    bm = _masks_for([[1, 0, 1, 0, 0, 1, 1]], 1)[0, 2]
+    for i in range(n):
+        want = [u for u in range(n * b) if u // b <= i and bm[i, u // b]]
+        assert oracle.kept_keys(bm, b, i).tolist() == want
+
+
+def test_kblock_matches_torch_autograd_on_long_columns():
+    # every block literal and w = 0 in the literal class: column j is kept by every
+    # query block i >= j, so column 0 has n entries
+    b, n, d = 4, 12, 8
+    bm = _masks_for([[1] * n], 0)
+    q, k, v, do = (_rand((1, 1, n * b, d), s) for s in (36, 37, 38, 39))
+    sc = 0.29
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    a = oracle.token_mask(bm[0, 1], b)
+    out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(a), scale=sc)
+    out.backward(torch.from_numpy(do))
+    for j in (0, 1, n // 2, n - 1):
+        gk, gv = oracle.attn_bwd_kblock(q[0, 0], k[0, 0], v[0, 0], do[0, 0], bm[0, 1], b, j, scale=sc)
+        sl = slice(j * b, (j + 1) * b)
+        np.testing.assert_allclose(gk, tk.grad.numpy()[0, 0, sl], atol=1e-12)
+        np.testing.assert_allclose(gv, tv.grad.numpy()[0, 0, sl], atol=1e-12)
