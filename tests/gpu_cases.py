@@ -97,6 +97,18 @@ def run_path(x_bytes, block, window, n_heads, tensors, backward, device="cuda"):
     return out
 
 
+def oracle_map(fn, jobs, workers: int = 8):
+    """[fn(*job) for job in jobs], run on a thread pool with one BLAS thread per worker:
+    the oracle's NumPy work releases the GIL, so independent blocks run side by side."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    if len(jobs) <= 1:
+        return [fn(*job) for job in jobs]
+    with threadpool_limits(1), ThreadPoolExecutor(min(workers, len(jobs))) as ex:
+        return list(ex.map(lambda job: fn(*job), jobs))
+
+
 def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
@@ -110,6 +122,6 @@ def max_err(got, ref):
 def assert_close(name, got, ref, tol):
     err = max_err(got, ref)
     log(f"    {name}: max|err| = {err:.3e}  max|ref| = {float(np.max(np.abs(ref))) if np.size(ref) else 0:.3e}"
-        f"  tol = {tol:.1e}")
+        f"  tol = {tol:.1e}  margin = {tol - err:.3e}")
     assert np.all(np.isfinite(got)), name
     assert err <= tol, f"{name}: {err} > {tol}"

@@ -14,7 +14,7 @@ import torch
 import content_adaptive_block_amd as gsa
 import oracle
 import synth
-from gpu_cases import BF16_TOL, F32_TOL, assert_close, check_mask, f64, log, run_path
+from gpu_cases import BF16_TOL, F32_TOL, assert_close, check_mask, f64, log, oracle_map, run_path
 
 pytestmark = pytest.mark.gpu
 
@@ -179,8 +179,11 @@ def test_locality_outside_kept_blocks():
 
 
 # ------------------------------------------------------------------ full config sizes
-def _sample_blocks(masks, n_heads, rng, by_columns, limit_len=None):
-    """A few (s, h, block) per class: first, last, a literal-heavy one and a random one."""
+def _sample_blocks(masks, n_heads, rng, by_columns):
+    """A few (s, h, block) per (sample, class): the first and last blocks, a random one
+    and the two with the longest lists (CSR rows, or CSC columns with ``by_columns``).
+    At config 5 the longest columns are the literal blocks of the sample with L = 211,
+    kept by up to 211 query blocks (the L^2 term of the edge count)."""
     classes = oracle.head_classes(n_heads)
     b, _, n, _ = masks.shape
     picks = []
@@ -190,17 +193,18 @@ def _sample_blocks(masks, n_heads, rng, by_columns, limit_len=None):
             if not hs:
                 continue
             lens = masks[s, cls].sum(axis=0 if by_columns else 1)
-            cand = {0, n - 1, int(rng.integers(n))}
             order = np.argsort(-lens, kind="stable")
-            for idx in order:
-                if limit_len is None or lens[idx] <= limit_len:
-                    cand.add(int(idx))
-                    break
+            cand = {0, n - 1, int(rng.integers(n))} | {int(x) for x in order[:2]}
             for blk in sorted(cand):
-                if limit_len is not None and lens[blk] > limit_len:
-                    continue
-                picks.append((s, hs[int(rng.integers(len(hs)))], blk))
+                picks.append((s, hs[int(rng.integers(len(hs)))], blk, int(lens[blk])))
     return picks
+
+
+def _compare_sampled(errs, ltol, tol):
+    for nm, pairs in errs.items():
+        got = np.concatenate([p[0].ravel() for p in pairs])
+        ref = np.concatenate([p[1].ravel() for p in pairs])
+        assert_close(f"{nm} ({len(pairs)} sampled blocks)", got, ref, ltol if nm == "LSE" else tol)
 
 
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
@@ -219,30 +223,51 @@ def test_full_size_sampled(cid):
     classes = oracle.head_classes(wl.n_heads)
     rng = np.random.default_rng(cid)
     tol, ltol = BF16_TOL, 1e-3
-    errs = {}
-    for s, h, i in _sample_blocks(masks, wl.n_heads, rng, by_columns=False):
+    heads = {}
+
+    def head(s, h):
+        if (s, h) not in heads:
+            heads[s, h] = tuple(f64(t[nm][s, h]) for nm in names)
+        return heads[s, h]
+
+    rows = _sample_blocks(masks, wl.n_heads, rng, by_columns=False)
+    log(f"    rows: {len(rows)} sampled, longest {max(r[3] for r in rows)} entries")
+
+    def row_ref(s, h, i, _len):
         bm = masks[s, classes[h]]
-        q, k, v = (f64(t[nm][s, h]) for nm in ("q", "k", "v"))
-        rows = np.arange(i * block, (i + 1) * block)
-        ro, rl = oracle.attn_fwd_rows(q, k, v, bm, block, rows)
-        errs.setdefault("O", []).append((f64(res["o"][s, h, i * block:(i + 1) * block]), ro))
-        errs.setdefault("LSE", []).append((f64(res["lse"][s, h, i * block:(i + 1) * block]), rl))
+        hv = head(s, h)
+        ro, rl = oracle.attn_fwd_rows(hv[0], hv[1], hv[2], bm, block, np.arange(i * block, (i + 1) * block))
+        rq = oracle.attn_bwd_qblock(*hv, bm, block, i) if wl.backward else None
+        return ro, rl, rq
+
+    for s, h, i in [r[:3] for r in rows]:
+        head(s, h)
+    errs = {}
+    for (s, h, i, _), (ro, rl, rq) in zip(rows, oracle_map(row_ref, rows)):
+        sl = slice(i * block, (i + 1) * block)
+        errs.setdefault("O", []).append((f64(res["o"][s, h, sl]), ro))
+        errs.setdefault("LSE", []).append((f64(res["lse"][s, h, sl]), rl))
         if wl.backward:
-            do = f64(t["do"][s, h])
-            rq = oracle.attn_bwd_qblock(q, k, v, do, bm, block, i)
-            errs.setdefault("dQ", []).append((f64(res["dq"][s, h, i * block:(i + 1) * block]), rq))
+            errs.setdefault("dQ", []).append((f64(res["dq"][s, h, sl]), rq))
     if wl.backward:
-        limit = 12 if cid == 5 else None
-        for s, h, j in _sample_blocks(masks, wl.n_heads, rng, by_columns=True, limit_len=limit):
-            bm = masks[s, classes[h]]
-            q, k, v, do = (f64(t[nm][s, h]) for nm in ("q", "k", "v", "do"))
-            rk, rv = oracle.attn_bwd_kblock(q, k, v, do, bm, block, j)
-            errs.setdefault("dK", []).append((f64(res["dk"][s, h, j * block:(j + 1) * block]), rk))
-            errs.setdefault("dV", []).append((f64(res["dv"][s, h, j * block:(j + 1) * block]), rv))
-    for nm, pairs in errs.items():
-        got = np.concatenate([p[0].ravel() for p in pairs])
-        ref = np.concatenate([p[1].ravel() for p in pairs])
-        assert_close(f"{nm} ({len(pairs)} sampled blocks)", got, ref, ltol if nm == "LSE" else tol)
+        cols = _sample_blocks(masks, wl.n_heads, rng, by_columns=True)
+        log(f"    columns: {len(cols)} sampled, lengths {sorted(c[3] for c in cols)[-6:]} (longest six)")
+        for s, h, j, _ in cols:
+            head(s, h)
+
+        def col_ref(s, h, j, _len):
+            return oracle.attn_bwd_kblock(*head(s, h), masks[s, classes[h]], block, j)
+
+        for (s, h, j, n_entries), (rk, rv) in zip(cols, oracle_map(col_ref, cols)):
+            sl = slice(j * block, (j + 1) * block)
+            errs.setdefault("dK", []).append((f64(res["dk"][s, h, sl]), rk))
+            errs.setdefault("dV", []).append((f64(res["dv"][s, h, sl]), rv))
+            if n_entries > 64:   # past the first 64-entry chunk of the column's list
+                errs.setdefault("dK (columns > 64 entries)", []).append(errs["dK"][-1])
+                errs.setdefault("dV (columns > 64 entries)", []).append(errs["dV"][-1])
+        if cid == 5:
+            assert "dV (columns > 64 entries)" in errs
+    _compare_sampled(errs, ltol, tol)
 
 
 @pytest.mark.parametrize("inst", list(BASE))
@@ -285,17 +310,19 @@ def test_backward_stage_entry_points(inst):
 
 
 DENSE = [
-    # (instance, batch, N, heads): window N - 1 and every head local = dense causal
+    # (instance, batch, N, heads): window N - 1 and every head local = dense causal; N > 65
+    # so that key block 0's column (N entries) runs past the first 64-entry list chunk
     (("bf16", 64, 64), 1, 128, 2),
-    (("bf16", 128, 128), 1, 64, 2),
-    (("f32", 16, 32), 2, 64, 2),
+    (("bf16", 128, 128), 1, 80, 2),
+    (("f32", 16, 32), 2, 96, 2),
 ]
 
 
 @pytest.mark.parametrize("inst,batch,n,heads", DENSE)
 def test_dense_causal_sampled(inst, batch, n, heads):
     """Window >= N - 1 turns every local head into plain causal attention over up to N
-    kept blocks per list (lists longer than 64 entries included)."""
+    kept blocks per list (lists longer than 64 entries included: the first query block
+    and key block 0 of every head)."""
     dtype, block, hd = inst
     n_heads, window = (heads, 0, 0), n - 1
     log(f"  dense causal {dtype} b={block} d={hd} B={batch} N={n} H={heads}")
@@ -305,27 +332,36 @@ def test_dense_causal_sampled(inst, batch, n, heads):
     assert np.array_equal(masks[:, 0], np.broadcast_to(np.tril(np.ones((n, n), bool)), (batch, n, n)))
     tol, ltol = _tol(dtype)
     rng = np.random.default_rng(n)
-    errs = {}
+    hv = {(s, h): tuple(f64(t[nm][s, h]) for nm in ("q", "k", "v", "do")) for s in range(batch)
+          for h in range(heads)}
+    row_jobs, col_jobs = [], []
     for s in range(batch):
         for h in range(heads):
-            q, k, v, do = (f64(t[nm][s, h]) for nm in ("q", "k", "v", "do"))
-            bm = masks[s, 0]
-            for i in sorted({0, n - 1, int(rng.integers(n))}):
-                rows = np.arange(i * block, (i + 1) * block)
-                ro, rl = oracle.attn_fwd_rows(q, k, v, bm, block, rows)
-                errs.setdefault("O", []).append((f64(res["o"][s, h, rows]), ro))
-                errs.setdefault("LSE", []).append((f64(res["lse"][s, h, rows]), rl))
-                rq = oracle.attn_bwd_qblock(q, k, v, do, bm, block, i)
-                errs.setdefault("dQ", []).append((f64(res["dq"][s, h, rows]), rq))
-            for j in sorted({n - 1, n - 2, n - 1 - int(rng.integers(4))}):
-                rows = np.arange(j * block, (j + 1) * block)
-                rk, rv = oracle.attn_bwd_kblock(q, k, v, do, bm, block, j)
-                errs.setdefault("dK", []).append((f64(res["dk"][s, h, rows]), rk))
-                errs.setdefault("dV", []).append((f64(res["dv"][s, h, rows]), rv))
-    for nm, pairs in errs.items():
-        got = np.concatenate([p[0].ravel() for p in pairs])
-        ref = np.concatenate([p[1].ravel() for p in pairs])
-        assert_close(f"{nm} ({len(pairs)} sampled blocks)", got, ref, ltol if nm == "LSE" else tol)
+            row_jobs += [(s, h, i) for i in sorted({0, n - 1, int(rng.integers(n))})]
+            col_jobs += [(s, h, j) for j in sorted({0, 1, n - 1, n - 2, n - 1 - int(rng.integers(4))})]
+
+    def row_ref(s, h, i):
+        q, k, v, do = hv[s, h]
+        ro, rl = oracle.attn_fwd_rows(q, k, v, masks[s, 0], block, np.arange(i * block, (i + 1) * block))
+        return ro, rl, oracle.attn_bwd_qblock(q, k, v, do, masks[s, 0], block, i)
+
+    def col_ref(s, h, j):
+        return oracle.attn_bwd_kblock(*hv[s, h], masks[s, 0], block, j)
+
+    errs = {}
+    for (s, h, i), (ro, rl, rq) in zip(row_jobs, oracle_map(row_ref, row_jobs)):
+        rows = np.arange(i * block, (i + 1) * block)
+        errs.setdefault("O", []).append((f64(res["o"][s, h, rows]), ro))
+        errs.setdefault("LSE", []).append((f64(res["lse"][s, h, rows]), rl))
+        errs.setdefault("dQ", []).append((f64(res["dq"][s, h, rows]), rq))
+    for (s, h, j), (rk, rv) in zip(col_jobs, oracle_map(col_ref, col_jobs)):
+        rows = np.arange(j * block, (j + 1) * block)
+        errs.setdefault("dK", []).append((f64(res["dk"][s, h, rows]), rk))
+        errs.setdefault("dV", []).append((f64(res["dv"][s, h, rows]), rv))
+        if n - j > 64:
+            errs.setdefault("dK (columns > 64 entries)", []).append(errs["dK"][-1])
+            errs.setdefault("dV (columns > 64 entries)", []).append(errs["dV"][-1])
+    _compare_sampled(errs, ltol, tol)
 
 
 def test_maximum_blocks_sampled():
@@ -350,7 +386,7 @@ def test_maximum_blocks_sampled():
             errs.setdefault("LSE", []).append((f64(res["lse"][0, h, rows]), rl))
             errs.setdefault("dQ", []).append((f64(res["dq"][0, h, rows]), oracle.attn_bwd_qblock(q, k, v, do, bm, 64, i)))
         lens = bm.sum(axis=0)
-        for j in sorted({n - 1, int(np.argmin(np.where(lens > 1, lens, 10 ** 9)))}):
+        for j in sorted({n - 1, int(np.argmin(np.where(lens > 1, lens, 10 ** 9))), int(np.argmax(lens))}):
             rows = np.arange(j * 64, (j + 1) * 64)
             rk, rv = oracle.attn_bwd_kblock(q, k, v, do, bm, 64, j)
             errs.setdefault("dK", []).append((f64(res["dk"][0, h, rows]), rk))
@@ -386,6 +422,20 @@ def test_binding_rejects_mismatched_outputs():
         gsa.gsa_attn_bwd(q, k, v, o, lse, do, m, 64, workspace=torch.empty(3, device=q.device))
     with pytest.raises(ValueError):
         gsa.gsa_attn_bwd(q, k, v, o, None, do, m, 64)
+    torch.cuda.synchronize()
+
+
+def test_attention_refuses_an_unbuilt_mask():
+    # buffers from GsaMask.empty hold no lists until a mask call fills them
+    m = gsa.GsaMask.empty(1, 2, 1, (1, 1, 0), "cuda")
+    q = torch.zeros((1, 2, 128, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        gsa.gsa_attn_fwd(q, q, q, m, 64)
+    lse = torch.zeros(q.shape[:3], dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        gsa.gsa_attn_bwd(q, q, q, q, lse, q, m, 64)
+    gsa.gsa_build_mask(torch.full((1, 2), 30, dtype=torch.int32, device="cuda"), 1, (1, 1, 0), out=m)
+    gsa.gsa_attn_fwd(q, q, q, m, 64)
     torch.cuda.synchronize()
 
 
