@@ -13,7 +13,6 @@ of arXiv 2607.21752), sections 背景与主要改动 and 核心公式.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -21,7 +20,8 @@ import numpy as np
 import torch  # loaded first: libgsa binds to the HIP runtime torch has already mapped
 
 __all__ = [
-    "GsaError", "GsaMask", "PrepPool", "lib_path", "load_library", "gsa_prepare", "gsa_mask_sizes",
+    "GsaError", "GsaMask", "PrepPool", "lib_path", "load_library", "gsa_prepare", "gsa_mask_bytes",
+    "gsa_mask_sizes",
     "gsa_build_mask", "gsa_build_mask_from_blocks", "gsa_bigbird_blocks",
     "gsa_attn_fwd", "gsa_attn_bwd", "attention", "zlib_version", "default_head_counts",
     "GSA_OK", "GSA_ERR_ARG", "GSA_ERR_SHAPE", "GSA_ERR_ZLIB", "GSA_ERR_HIP", "GSA_ERR_UNSUPPORTED",
@@ -91,8 +91,11 @@ def load_library():
     lib.gsa_prep_pool_destroy.argtypes = [vp]
     for nm in ("gsa_prep_pool_create", "gsa_prep_pool_submit", "gsa_prep_pool_wait", "gsa_prep_pool_destroy"):
         getattr(lib, nm).restype = i32
-    lib.gsa_mask_sizes.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
-    lib.gsa_mask_sizes.restype = i32
+    for nm in ("gsa_mask_bytes", "gsa_mask_sizes"):
+        getattr(lib, nm).argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
+        getattr(lib, nm).restype = i32
+    lib.gsa_default_head_counts.argtypes = [i32, ctypes.POINTER(i32)]
+    lib.gsa_default_head_counts.restype = i32
     lib.gsa_build_mask.argtypes = [vp, ctypes.POINTER(_Mask), vp]
     lib.gsa_build_mask.restype = i32
     lib.gsa_build_mask_from_blocks.argtypes = [vp, ctypes.POINTER(_Mask), vp]
@@ -126,8 +129,11 @@ def zlib_version() -> str:
 
 
 def default_head_counts(heads: int):
-    """Half local, a quarter literal, the rest hybrid ([note] 背景与主要改动)."""
-    return (heads // 2, heads // 4, heads - heads // 2 - heads // 4)
+    """The library's default split of ``heads`` into (local, literal, hybrid) counts
+    (gsa_default_head_counts)."""
+    out = (ctypes.c_int32 * 3)()
+    _check(load_library().gsa_default_head_counts(heads, out), "gsa_default_head_counts")
+    return tuple(int(x) for x in out)
 
 
 def _stream_ptr(device) -> int:
@@ -214,16 +220,22 @@ class PrepPool:
 
 
 # ---------------------------------------------------------------------------------- (2)
-def gsa_mask_sizes(batch: int, n_blocks: int, n_heads) -> list:
+def gsa_mask_bytes(batch: int, n_blocks: int, n_heads) -> list:
+    """Byte sizes of the mask buffers, in ``MASK_FIELDS`` order."""
     nh = (ctypes.c_int32 * 3)(*n_heads)
-    sizes = (ctypes.c_size_t * 10)()
-    _check(load_library().gsa_mask_sizes(batch, n_blocks, nh, sizes), "gsa_mask_sizes")
+    sizes = (ctypes.c_size_t * len(MASK_FIELDS))()
+    _check(load_library().gsa_mask_bytes(batch, n_blocks, nh, sizes), "gsa_mask_bytes")
     return list(sizes)
+
+
+gsa_mask_sizes = gsa_mask_bytes
 
 
 @dataclass
 class GsaMask:
-    """Device-resident mask of one batch (buffers as in include/gsa.h)."""
+    """Device-resident mask of one batch (buffers as in include/gsa.h).  ``built`` is set
+    once a mask call has been enqueued into the buffers; the attention calls refuse a mask
+    whose buffers were never filled."""
     batch: int
     n_blocks: int
     window: int
@@ -238,12 +250,14 @@ class GsaMask:
     work_row: torch.Tensor
     work_col: torch.Tensor
     sched: torch.Tensor
+    built: bool = False
 
     @property
     def cap(self) -> int:
         return self.n_blocks * (self.n_blocks + 1) // 2
 
     def struct(self) -> _Mask:
+        """The C struct over these buffers (for mask and attention calls)."""
         m = _Mask()
         m.batch, m.n_blocks, m.window = self.batch, self.n_blocks, self.window
         m.n_heads[:] = list(self.n_heads)
@@ -281,6 +295,7 @@ def gsa_build_mask(c, window: int, n_heads, device=None, out: GsaMask | None = N
     ms = m.struct()
     _check(load_library().gsa_build_mask(c.data_ptr(), ctypes.byref(ms), _stream_ptr(device)),
            "gsa_build_mask")
+    m.built = True
     return m
 
 
@@ -299,6 +314,7 @@ def gsa_build_mask_from_blocks(blocks: torch.Tensor, n_heads, out: GsaMask | Non
     ms = m.struct()
     _check(load_library().gsa_build_mask_from_blocks(blocks.data_ptr(), ctypes.byref(ms), _stream_ptr(blocks.device)),
            "gsa_build_mask_from_blocks")
+    m.built = True
     return m
 
 
@@ -356,6 +372,11 @@ def _check_rows(t, ref, name):
         raise ValueError(f"{name} must be a contiguous float32 tensor {tuple(ref.shape[:3])} on {ref.device}")
 
 
+def _check_built(mask: GsaMask):
+    if not (isinstance(mask, GsaMask) and mask.built):
+        raise ValueError("the mask was never built: call gsa_build_mask or gsa_build_mask_from_blocks first")
+
+
 def _fwd_struct(q, k, v, o, lse, block, scale) -> _FwdArgs:
     a = _FwdArgs()
     a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)
@@ -368,6 +389,7 @@ def _fwd_struct(q, k, v, o, lse, block, scale) -> _FwdArgs:
 def gsa_attn_fwd(q, k, v, mask: GsaMask, block: int, scale: float = 0.0, with_lse: bool = True,
                  out=None, lse=None):
     """O [B, H, T, d] (and LSE fp32 [B, H, T]) of the gzip-masked causal attention."""
+    _check_built(mask)
     _check_tensors(q, k, v)
     o = torch.empty_like(q) if out is None else out
     _check_out(o, q, "out")
@@ -398,6 +420,7 @@ def gsa_attn_bwd(q, k, v, o, lse, dout, mask: GsaMask, block: int, scale: float 
     """dQ, dK, dV of sum(O * dout).  ``stage`` runs one backward stage only: "dq" (also
     writes D into ``workspace``), then "dkdv" (reads it); "prep" writes D alone, for
     running "dkdv" without "dq".  Stages share ``workspace`` and ``out``."""
+    _check_built(mask)
     _check_tensors(q, k, v, o, dout)
     if lse is not None or stage != "prep":   # the D-only stage reads no LSE
         _check_rows(lse, q, "lse")
@@ -433,7 +456,3 @@ class _GsaAttention(torch.autograd.Function):
 def attention(q, k, v, mask: GsaMask, block: int, scale: float = 0.0):
     """Differentiable gzip-masked attention (forward and backward through libgsa)."""
     return _GsaAttention.apply(q, k, v, mask, block, scale)
-
-
-def softmax_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)

@@ -23,7 +23,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIP_SOURCES = ["gsa_mask.hip", "gsa_attn_fwd.hip", "gsa_attn_bwd.hip"]
 # Compiled a second time with GSA_WIDE_TU defined: the 128 x 128 forward and dQ kernels.
 WIDE_SOURCES = ["gsa_attn_fwd.hip", "gsa_attn_bwd.hip"]
-CPP_SOURCES = ["gsa_api.cpp", "gsa_prepare.cpp"]
+CPP_SOURCES = ["gsa_api.cpp", "gsa_error.cpp", "gsa_prepare.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 # MFMA accumulators stay in ordinary VGPRs (no AGPR copies around every product).

@@ -1,28 +1,13 @@
-// C ABI entry points: argument validation, status strings and error reporting.
-// Every check here runs before any HIP call, so a rejected call has no side effects.
+// C ABI entry points: argument validation and kernel launches.  Every check here runs
+// before any HIP call, so a rejected call has no side effects.  Status strings and the
+// thread-local error detail live in gsa_error.cpp.
 #include <cstdio>
 #include <cstring>
 #include <string>
 
-#include <zlib.h>
-
 #include "gsa_internal.hpp"
 
 namespace gsa {
-
-static thread_local std::string g_last_error;
-
-gsa_status fail(gsa_status st, const char *fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return st;
-}
-
-void clear_error() { g_last_error.clear(); }
 
 gsa_status check_launch(const char *what) {
   hipError_t e = hipGetLastError();
@@ -87,25 +72,9 @@ using namespace gsa;
 
 extern "C" {
 
-const char *gsa_status_str(int32_t s) {
-  switch (s) {
-    case GSA_OK: return "GSA_OK";
-    case GSA_ERR_ARG: return "GSA_ERR_ARG";
-    case GSA_ERR_SHAPE: return "GSA_ERR_SHAPE";
-    case GSA_ERR_ZLIB: return "GSA_ERR_ZLIB";
-    case GSA_ERR_HIP: return "GSA_ERR_HIP";
-    case GSA_ERR_UNSUPPORTED: return "GSA_ERR_UNSUPPORTED";
-    default: return "GSA_ERR_UNKNOWN";
-  }
-}
-
-const char *gsa_last_error(void) { return g_last_error.c_str(); }
-
-const char *gsa_zlib_version(void) { return zlibVersion(); }
-
 int32_t gsa_abi_version(void) { return GSA_ABI_VERSION; }
 
-gsa_status gsa_mask_sizes(int64_t batch, int32_t n_blocks, const int32_t n_heads[3],
+gsa_status gsa_mask_bytes(int64_t batch, int32_t n_blocks, const int32_t n_heads[3],
                           size_t sizes_out[GSA_MASK_NBUF]) {
   clear_error();
   if (!n_heads || !sizes_out) return fail(GSA_ERR_ARG, "NULL argument");
@@ -125,6 +94,21 @@ gsa_status gsa_mask_sizes(int64_t batch, int32_t n_blocks, const int32_t n_heads
   sizes_out[7] = B * H * N * 16;             // work_row: 4 int32 per item
   sizes_out[8] = B * H * N * 16;             // work_col
   sizes_out[9] = (size_t)sched_words(batch, n_blocks) * 4;  // sched: work-order scratch
+  return GSA_OK;
+}
+
+gsa_status gsa_mask_sizes(int64_t batch, int32_t n_blocks, const int32_t n_heads[3],
+                          size_t sizes_out[GSA_MASK_NBUF]) {
+  return gsa_mask_bytes(batch, n_blocks, n_heads, sizes_out);
+}
+
+gsa_status gsa_default_head_counts(int32_t heads, int32_t n_heads_out[3]) {
+  clear_error();
+  if (!n_heads_out) return fail(GSA_ERR_ARG, "n_heads_out is NULL");
+  if (heads < 0) return fail(GSA_ERR_ARG, "heads %d < 0", heads);
+  n_heads_out[0] = heads / 2;
+  n_heads_out[1] = heads / 4;
+  n_heads_out[2] = heads - heads / 2 - heads / 4;
   return GSA_OK;
 }
 

@@ -160,9 +160,23 @@ typedef struct {
 
 #define GSA_MASK_NBUF 10
 
-/* Byte sizes of the ten mask buffers, in the struct's field order (flags .. sched). */
+/* Byte sizes of the GSA_MASK_NBUF mask buffers, in the struct's field order (flags ..
+ * sched), for a caller that allocates them.  The work list is two descriptor arrays
+ * (rows for the forward and dQ, columns for dK/dV) plus the sched scratch that builds
+ * them, hence ten buffers.
+ * Errors: NULL n_heads/sizes_out, negative batch, n_blocks or head count -> GSA_ERR_ARG. */
+gsa_status gsa_mask_bytes(int64_t batch, int32_t n_blocks, const int32_t n_heads[3],
+                          size_t sizes_out[GSA_MASK_NBUF]);
+/* The same as gsa_mask_bytes (earlier name, kept for existing callers). */
 gsa_status gsa_mask_sizes(int64_t batch, int32_t n_blocks, const int32_t n_heads[3],
                           size_t sizes_out[GSA_MASK_NBUF]);
+
+/* Default head split of [note] 背景与主要改动: half of the heads local, a quarter
+ * literal, the rest hybrid, i.e. (floor(H/2), floor(H/4), H - floor(H/2) - floor(H/4));
+ * for H = 4, 12, 16 this is (2,1,1), (6,3,3), (8,4,4).  Callers may pass any other
+ * split to the mask and attention calls.
+ * Errors: heads < 0 or NULL n_heads_out -> GSA_ERR_ARG. */
+gsa_status gsa_default_head_counts(int32_t heads, int32_t n_heads_out[3]);
 
 /* Fills every buffer of *m from c_dev (device, int32 [B, N], lengths from gsa_prepare).
  * Errors: NULL pointers, window < 0, negative head counts -> GSA_ERR_ARG;

@@ -24,7 +24,8 @@ def test_exports_every_declared_symbol(lib):
     text = open(os.path.join(ROOT, "include", "gsa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = set(re.findall(r"\b(gsa_[a-z_]+)\s*\(", text))
-    assert {"gsa_prepare", "gsa_build_mask", "gsa_attn_fwd", "gsa_attn_bwd", "gsa_mask_sizes"} <= names
+    assert {"gsa_prepare", "gsa_build_mask", "gsa_attn_fwd", "gsa_attn_bwd", "gsa_mask_bytes", "gsa_mask_sizes",
+            "gsa_default_head_counts"} <= names
     for nm in sorted(names):
         assert hasattr(lib, nm), nm
     assert lib.gsa_abi_version() == 1
@@ -71,13 +72,34 @@ def test_prepare_errors(lib):
     assert gsa.gsa_prepare(np.zeros((0, 64), np.uint8), 16).shape == (0, 4)
 
 
-def test_mask_sizes():
-    sizes = gsa.gsa_mask_sizes(2, 5, (2, 1, 1))
+def test_mask_bytes(lib):
+    sizes = gsa.gsa_mask_bytes(2, 5, (2, 1, 1))
     cap = 15
     assert sizes == [10, 8, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 6 * 4, 2 * 3 * cap * 4, 2 * 3 * 8,
                      2 * 4 * 5 * 16, 2 * 4 * 5 * 16, 2 * 3 * 2 * (5 + 32) * 4]
+    assert gsa.gsa_mask_sizes(3, 128, (6, 3, 3)) == gsa.gsa_mask_bytes(3, 128, (6, 3, 3))
     with pytest.raises(gsa.GsaError):
-        gsa.gsa_mask_sizes(-1, 5, (1, 1, 1))
+        gsa.gsa_mask_bytes(-1, 5, (1, 1, 1))
+    with pytest.raises(gsa.GsaError):
+        gsa.gsa_mask_bytes(1, 5, (1, -1, 1))
+    # straight through the C ABI: ten sizes, NULL arguments rejected
+    nh = (ctypes.c_int32 * 3)(6, 3, 3)
+    out = (ctypes.c_size_t * 10)()
+    assert lib.gsa_mask_bytes(8, 128, nh, out) == gsa.GSA_OK
+    assert list(out)[7] == 8 * 12 * 128 * 16
+    assert lib.gsa_mask_bytes(8, 128, None, out) == gsa.GSA_ERR_ARG
+    assert lib.gsa_mask_bytes(8, 128, nh, None) == gsa.GSA_ERR_ARG
+
+
+def test_default_head_counts(lib):
+    # [note] 背景与主要改动: half local, a quarter literal, the rest hybrid; the library's
+    # split agrees with the oracle's on every head count
+    for h in range(0, 40):
+        assert gsa.default_head_counts(h) == oracle.default_head_counts(h)
+    assert gsa.default_head_counts(12) == (6, 3, 3)
+    with pytest.raises(gsa.GsaError):
+        gsa.default_head_counts(-1)
+    assert lib.gsa_default_head_counts(4, None) == gsa.GSA_ERR_ARG
 
 
 FAKE = 0x10000   # a non-NULL, aligned address: validation must fail before it is used
