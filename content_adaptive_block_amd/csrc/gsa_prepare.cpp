@@ -23,6 +23,25 @@
 
 #include "gsa_internal.hpp"
 
+#ifdef GSA_TEST_HOOKS
+// Test builds only (the library is never built with GSA_TEST_HOOKS): deflate's
+// allocations succeed while a countdown lasts and then fail, so that the zlib error path
+// of the host stage can be reached.  gsa_test_fail_zalloc_after(n) lets n more
+// allocations succeed; n < 0 switches the failures off.
+#include <cstdlib>
+static std::atomic<long> g_zalloc_left{-1};
+extern "C" void gsa_test_fail_zalloc_after(long n) { g_zalloc_left.store(n); }
+static voidpf test_zalloc(voidpf, uInt items, uInt size) {
+  long left = g_zalloc_left.load();
+  while (left >= 0) {
+    if (left == 0) return Z_NULL;
+    if (g_zalloc_left.compare_exchange_weak(left, left - 1)) break;
+  }
+  return calloc(items, size);
+}
+static void test_zfree(voidpf, voidpf p) { free(p); }
+#endif
+
 namespace {
 
 struct BlockDeflater {
@@ -31,6 +50,10 @@ struct BlockDeflater {
   std::vector<unsigned char> out;
 
   explicit BlockDeflater(uLong max_in) {
+#ifdef GSA_TEST_HOOKS
+    zs.zalloc = test_zalloc;
+    zs.zfree = test_zfree;
+#endif
     // level 1, deflate, windowBits 15 + 16 (gzip wrapper), memLevel 8, default strategy.
     init_err = deflateInit2(&zs, 1, Z_DEFLATED, 15 + 16, 8, Z_DEFAULT_STRATEGY);
     if (init_err == Z_OK) out.resize(deflateBound(&zs, max_in) + 64);
