@@ -249,12 +249,17 @@ class DevicePath:
             gsa.gsa_build_mask(self.c_dev, wl.window, wl.n_heads, out=self.mask)
         if ev is not None:
             ev[1].record(self.stream)
-        gsa.gsa_attn_fwd(t["q"], t["k"], t["v"], self.mask, wl.block, out=self.o, lse=self.lse)
+        self.attention(self.mask, ev)
+
+    def attention(self, mask, ev=None):
+        """Forward, then (backward workloads) dQ and dK/dV through ``mask``."""
+        gsa, wl, t = self.gsa, self.wl, self.t
+        gsa.gsa_attn_fwd(t["q"], t["k"], t["v"], mask, wl.block, out=self.o, lse=self.lse)
         if ev is not None:
             ev[2].record(self.stream)
         if wl.backward:
             for i, stage in enumerate(("dq", "dkdv")):
-                gsa.gsa_attn_bwd(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], self.mask, wl.block,
+                gsa.gsa_attn_bwd(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], mask, wl.block,
                                  workspace=self.ws, out=self.grads, stage=stage)
                 if ev is not None:
                     ev[3 + i].record(self.stream)
@@ -413,42 +418,34 @@ def main():
                                for i, nm in enumerate(path.kernels)}}
 
     # Host-stage pipeline: the gzip sizes of batch k + 1 are computed by the persistent
-    # pool while the device runs batch k, against the serial order (sizes, then device).
+    # pool while the device runs batch k (MaskPipeline), against the serial order (sizes,
+    # upload, mask, attention, wait).
     pipeline = None
     if args.pipeline_steps > 0:
+        from content_adaptive_block_amd.pipeline import MaskPipeline
         xs = [x, np.ascontiguousarray(np.roll(x, wl.block, axis=1))]   # two batches, masks differ
-        bufs = [torch.empty(c.shape, dtype=torch.int32).pin_memory() for _ in xs]
+        batches = [xs[k % 2] for k in range(args.pipeline_steps)]
         threads = max(1, (os.cpu_count() or 2) - 1)
-        saved = path.c_host
-        k_steps = args.pipeline_steps
+        k_steps = len(batches)
+        c_pin = torch.empty(c.shape, dtype=torch.int32).pin_memory()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for k in range(k_steps):
-            bufs[k % 2].numpy()[...] = gsa.gsa_prepare(xs[k % 2], wl.block, n_threads=threads)
-            path.c_host = bufs[k % 2]
-            path.step(upload=True)
+        for xb in batches:
+            c_pin.numpy()[...] = gsa.gsa_prepare(xb, wl.block, n_threads=threads)
+            path.c_dev.copy_(c_pin, non_blocking=True)
+            gsa.gsa_build_mask(path.c_dev, wl.window, wl.n_heads, out=path.mask)
+            path.attention(path.mask)
             torch.cuda.synchronize()
         serial = (time.perf_counter() - t0) / k_steps * 1e3
-        with gsa.PrepPool(threads) as pool:
-            pool.submit(xs[0], wl.block, bufs[0])
-            pool.wait()
-            prev = None
+        with MaskPipeline(wl.batch, wl.seq_len, wl.block, wl.window, wl.n_heads, dev, threads) as pipe:
+            pipe.run(batches[:2], lambda k, m: path.attention(m))
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            for k in range(k_steps):
-                path.c_host = bufs[k % 2]
-                path.step(upload=True)
-                done = torch.cuda.Event()
-                done.record(path.stream)
-                if prev is not None:
-                    prev.synchronize()   # batch k - 1 (the other buffer's copy) has finished
-                if k + 1 < k_steps:
-                    pool.submit(xs[(k + 1) % 2], wl.block, bufs[(k + 1) % 2])
-                    pool.wait()
-                prev = done
+            pipe.run(batches, lambda k, m: path.attention(m))
             torch.cuda.synchronize()
             pipelined = (time.perf_counter() - t0) / k_steps * 1e3
-        path.c_host = saved
+        path.c_dev.copy_(path.c_host)
+        torch.cuda.synchronize()
         pipeline = {"batches": k_steps, "host_threads": threads, "serial_ms_per_batch": round(serial, 4),
                     "pipelined_ms_per_batch": round(pipelined, 4), "device_ms_per_step": round(ms_step, 4)}
 
