@@ -22,7 +22,7 @@ import torch  # loaded first: libgsa binds to the HIP runtime torch has already 
 __all__ = [
     "GsaError", "GsaMask", "PrepPool", "lib_path", "load_library", "gsa_prepare", "gsa_mask_bytes",
     "gsa_mask_sizes",
-    "gsa_build_mask", "gsa_build_mask_from_blocks", "gsa_bigbird_blocks",
+    "gsa_build_mask", "gsa_build_mask_noalloc", "gsa_build_mask_from_blocks", "gsa_bigbird_blocks",
     "gsa_attn_fwd", "gsa_attn_bwd", "attention", "zlib_version", "default_head_counts",
     "GSA_OK", "GSA_ERR_ARG", "GSA_ERR_SHAPE", "GSA_ERR_ZLIB", "GSA_ERR_HIP", "GSA_ERR_UNSUPPORTED",
 ]
@@ -98,6 +98,8 @@ def load_library():
     lib.gsa_default_head_counts.restype = i32
     lib.gsa_build_mask.argtypes = [vp, ctypes.POINTER(_Mask), vp]
     lib.gsa_build_mask.restype = i32
+    lib.gsa_build_mask_noalloc.argtypes = [vp, ctypes.POINTER(_Mask), vp]
+    lib.gsa_build_mask_noalloc.restype = i32
     lib.gsa_build_mask_from_blocks.argtypes = [vp, ctypes.POINTER(_Mask), vp]
     lib.gsa_build_mask_from_blocks.restype = i32
     lib.gsa_bigbird_blocks.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp]
@@ -297,6 +299,27 @@ def gsa_build_mask(c, window: int, n_heads, device=None, out: GsaMask | None = N
            "gsa_build_mask")
     m.built = True
     return m
+
+
+def gsa_build_mask_noalloc(c: torch.Tensor, window: int, n_heads, out: GsaMask) -> GsaMask:
+    """gsa_build_mask for callers that cannot allocate device memory: ``c`` must already
+    be a contiguous device int32 tensor [B, N] and ``out`` a mask of that shape; its
+    ``sched`` buffer is not used (the library's own scratch array serves instead).
+    Nothing is allocated here or in the library."""
+    if not (isinstance(c, torch.Tensor) and c.is_cuda and c.dtype == torch.int32 and c.dim() == 2
+            and c.is_contiguous()):
+        raise ValueError("c must be a contiguous device int32 tensor [batch, n_blocks]")
+    if not isinstance(out, GsaMask):
+        raise ValueError("out must be a preallocated GsaMask")
+    batch, n = c.shape
+    if (out.batch, out.n_blocks) != (batch, n) or out.n_heads != tuple(int(h) for h in n_heads):
+        raise ValueError("preallocated mask has another shape or head split")
+    out.window = window
+    ms = out.struct()
+    _check(load_library().gsa_build_mask_noalloc(c.data_ptr(), ctypes.byref(ms), _stream_ptr(c.device)),
+           "gsa_build_mask_noalloc")
+    out.built = True
+    return out
 
 
 def gsa_build_mask_from_blocks(blocks: torch.Tensor, n_heads, out: GsaMask | None = None) -> GsaMask:

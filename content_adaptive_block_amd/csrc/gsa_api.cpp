@@ -17,7 +17,8 @@ gsa_status check_launch(const char *what) {
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-static gsa_status check_mask(const gsa_mask *m, bool building) {
+// building: the call fills the mask (flags, counts and, unless own_sched, sched needed).
+static gsa_status check_mask(const gsa_mask *m, bool building, bool own_sched = false) {
   if (!m) return fail(GSA_ERR_ARG, "mask is NULL");
   if (m->batch < 0) return fail(GSA_ERR_ARG, "mask batch %lld < 0", (long long)m->batch);
   if (m->window < 0) return fail(GSA_ERR_ARG, "window %d < 0", m->window);
@@ -30,9 +31,11 @@ static gsa_status check_mask(const gsa_mask *m, bool building) {
     return fail(GSA_ERR_ARG, "mask list buffer is NULL");
   if (!aligned16(m->work_row) || !aligned16(m->work_col))
     return fail(GSA_ERR_ARG, "mask work buffers are not 16-byte aligned");
-  if (building && (!m->flags || !m->n_literal || !m->n_edges || !m->sched))
-    return fail(GSA_ERR_ARG, "mask flag/count/sched buffer is NULL");
-  if (building && !aligned16(m->sched)) return fail(GSA_ERR_ARG, "mask sched buffer is not 16-byte aligned");
+  if (building && (!m->flags || !m->n_literal || !m->n_edges))
+    return fail(GSA_ERR_ARG, "mask flag/count buffer is NULL");
+  if (building && !own_sched && !m->sched) return fail(GSA_ERR_ARG, "mask sched buffer is NULL");
+  if (building && !own_sched && !aligned16(m->sched))
+    return fail(GSA_ERR_ARG, "mask sched buffer is not 16-byte aligned");
   int64_t items = m->batch * (int64_t)(m->n_heads[0] + m->n_heads[1] + m->n_heads[2]) * m->n_blocks;
   if (items > INT32_MAX) return fail(GSA_ERR_UNSUPPORTED, "B*H*N = %lld exceeds int32", (long long)items);
   return GSA_OK;
@@ -119,6 +122,21 @@ gsa_status gsa_build_mask(const int32_t *c_dev, const gsa_mask *m, hipStream_t s
   if (m->batch == 0) return GSA_OK;
   if (!c_dev) return fail(GSA_ERR_ARG, "c_dev is NULL");
   return launch_build_mask(c_dev, *m, stream);
+}
+
+gsa_status gsa_build_mask_noalloc(const int32_t *c_dev, const gsa_mask *m, hipStream_t stream) {
+  clear_error();
+  gsa_status st = check_mask(m, true, true);
+  if (st != GSA_OK) return st;
+  if (m->batch == 0) return GSA_OK;
+  if (!c_dev) return fail(GSA_ERR_ARG, "c_dev is NULL");
+  const int64_t need = sched_words(m->batch, m->n_blocks) * 4;
+  if (need > (int64_t)GSA_NOALLOC_SCHED_BYTES)
+    return fail(GSA_ERR_UNSUPPORTED,
+                "batch %lld x %d blocks needs %lld bytes of work-order scratch; gsa_build_mask_noalloc "
+                "holds %u (use gsa_build_mask with a caller-allocated sched buffer)",
+                (long long)m->batch, m->n_blocks, (long long)need, (unsigned)GSA_NOALLOC_SCHED_BYTES);
+  return launch_build_mask_noalloc(c_dev, *m, stream);
 }
 
 gsa_status gsa_build_mask_from_blocks(const uint8_t *blocks_dev, const gsa_mask *m, hipStream_t stream) {

@@ -19,6 +19,8 @@ gsa_status check_launch(const char *what);
 
 // Kernel launchers (arguments already validated).
 gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t stream);
+// gsa_build_mask with the work-order scratch in the library's static device array.
+gsa_status launch_build_mask_noalloc(const int32_t *c, const gsa_mask &m, hipStream_t stream);
 gsa_status launch_mask_from_blocks(const uint8_t *blocks, const gsa_mask &m, hipStream_t stream);
 gsa_status launch_bigbird(int64_t batch, int32_t n, int32_t window, int32_t n_global, int32_t n_random,
                           const int32_t *rnd, uint8_t *blocks, hipStream_t stream);

@@ -31,6 +31,8 @@
 // kernel 2 (one workgroup per list) scans hist over keys and segments into base; kernel 3
 // places every item with one thread, as a descriptor (item, beg, end, first entry) that
 // the attention kernels read with one load.
+#include <mutex>
+
 #include "gsa_device.hpp"
 #include "gsa_internal.hpp"
 
@@ -591,6 +593,56 @@ gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t st
   gsa_status st = check_launch("mask_kernel");
   if (st != GSA_OK) return st;
   return launch_order(m, stream);
+}
+
+// Work-order scratch of gsa_build_mask_noalloc: a file-scope device array, one copy per
+// GPU.  In host code `scratch` names a host-side stand-in, not the device memory, so the
+// kernels get its device address, looked up once per device (with that device current)
+// by hipGetSymbolAddress and kept in g_scratch.  Every entry of the scratch is written
+// by the mask kernel or the order kernels before it is read, so nothing needs clearing
+// between calls.
+static __device__ __align__(256) int32_t scratch[GSA_NOALLOC_SCHED_BYTES / 4];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch[kMaxDevices] = {};
+
+gsa_status scratch_on(int dev, int32_t **out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(GSA_ERR_UNSUPPORTED, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(GSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(GSA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess)
+        return fail(GSA_ERR_HIP, "hipSetDevice(%d): %s", cur, hipGetErrorString(e2));
+    }
+    if (e != hipSuccess || !p)
+      return fail(GSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev] = static_cast<int32_t *>(p);
+  }
+  *out = g_scratch[dev];
+  return GSA_OK;
+}
+}  // namespace
+
+gsa_status launch_build_mask_noalloc(const int32_t *c, const gsa_mask &m, hipStream_t stream) {
+  int dev = 0;
+  const hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return fail(GSA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  int32_t *ptr = nullptr;
+  gsa_status st = scratch_on(dev, &ptr);
+  if (st != GSA_OK) return st;
+  gsa_mask mm = m;
+  mm.sched = ptr;
+  return launch_build_mask(c, mm, stream);
 }
 
 gsa_status launch_mask_from_blocks(const uint8_t *blocks, const gsa_mask &m, hipStream_t stream) {

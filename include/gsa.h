@@ -184,6 +184,23 @@ gsa_status gsa_default_head_counts(int32_t heads, int32_t n_heads_out[3]);
 gsa_status gsa_build_mask(const int32_t *c_dev, const gsa_mask *m, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * (2') gsa_build_mask for callers that cannot allocate device memory (code under HIP graph
+ *      capture, tight serving loops, harnesses that forbid allocation).
+ *
+ *   Same arguments, outputs and errors as gsa_build_mask, except that m->sched is not
+ *   used (it may be NULL): the work-order scratch lives in a library-owned device array
+ *   of GSA_NOALLOC_SCHED_BYTES, one per GPU, placed when the library is loaded and held
+ *   until the process ends.  The call allocates nothing (no hipMalloc, no allocating
+ *   library routine); the first call on a device looks the array's address up once.
+ *   Every call on one GPU shares that array and leaves its last contents there; calls
+ *   that overlap on one GPU (concurrent streams or host threads) race on it.
+ * Extra error: a batch whose scratch (2 * 3 * batch * (N + 32) int32 words) exceeds
+ * GSA_NOALLOC_SCHED_BYTES -> GSA_ERR_UNSUPPORTED, before anything is enqueued.
+ * ------------------------------------------------------------------------------------ */
+#define GSA_NOALLOC_SCHED_BYTES (2u << 20)
+gsa_status gsa_build_mask_noalloc(const int32_t *c_dev, const gsa_mask *m, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * (2b) Lists of a caller-given block mask, for comparisons with other block-sparse
  *      patterns through the same attention kernels (the pages compare the method with
  *      BigBird: [note] 论文离线与线上效果).
