@@ -7,16 +7,26 @@ backward stages (dQ, which also forms D, then dK/dV).  The host gzip stage
 (gsa_prepare) and the PCIe hand-over of its sizes are timed separately
 (``host_prepare_ms``, ``c_upload_ms``, ``ms_per_step_with_upload``).
 
-The workload is 8 samples x 8192 bytes, block 64, window 2, 12 heads (6 local /
+The headline workload is 8 samples x 8192 bytes, block 64, window 2, 12 heads (6 local /
 3 literal / 3 hybrid), head_dim 64, bf16, forward + backward, on seeded synthetic
 text-like bytes (the pages' PG-19 runs at 8K bytes are the shape it stands in for).
 
+Timing: the primary figures are cold-cache steps.  Before each step a 512 MiB buffer
+(larger than the 256 MB Infinity Cache) is written, outside the events that time the
+step; HIP events on the launch stream mark the step's start and the end of every
+kernel.  The device first runs ``--settle-ms`` of such steps untimed (its clocks settle
+under sustained load), then ``--warmup`` steps, then ``--steps`` timed steps; the step
+time is their median.  ``warm`` gives the same for back-to-back steps with nothing in
+between (secondary).
+
 Prints ONE JSON line.  ``value`` is effective TFLOP/s on kept blocks: algorithmic
 FLOPs (4 b^2 d per kept tile forward, 10 b^2 d backward, diagonal tiles counted whole)
-divided by the step time.  ``roofline`` rates the kernel that takes the most time per
-step against its binding MI355X roof, from HIP events around each kernel on its stream;
-``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload and
-compares the timed step's outputs on that sample with it (``cpu_baseline.parity``);
+divided by the cold step time.  ``roofline`` rates the kernel that takes the most time per
+cold step against its binding MI355X roof; ``cpu_baseline`` times the fp64 CPU oracle on
+a bounded sample of the same workload, one (sample, head) per worker process with one
+BLAS thread each, and compares the timed step's outputs on that sample with it
+(``cpu_baseline.parity``); ``configs`` holds the same step and roofline figures for the
+other workloads (tiny fp32, 8 x 4 KiB, 8 x 8 KiB forward, 2 x 64 KiB forward+backward);
 ``env`` names the GPU, HIP, torch and zlib versions and the seeds.
 """
 from __future__ import annotations
@@ -154,61 +164,161 @@ def record_traffic(args, fetch_csv: str, write_csv: str):
     print(f"\nscale: FETCH x {scale_f:.4f}, WRITE x {scale_w:.4f} (copy of {args.copy_mib} MiB)")
 
 
-def cpu_baseline(wl, x_bytes, tensors, device_out, budget_s: float):
-    """The fp64 oracle on whole heads of sample 0 until ``budget_s`` seconds are spent.
+def _demangle(name: str) -> str:
+    """Readable form of a mangled kernel name: its nested name and template arguments
+    (bf16 / float types and integer values), e.g. gsa::attn_fwd_kernel<bf16, 64, 64>."""
+    import re
+    if not name.startswith("_ZN"):
+        return name
+    pos, parts = 3, []
+    while pos < len(name) and name[pos].isdigit():
+        m = re.match(r"\d+", name[pos:])
+        n = int(m.group())
+        pos += len(m.group())
+        ident = name[pos:pos + n]
+        pos += n
+        if not ident.startswith("_GLOBAL__N"):
+            parts.append(ident)
+    args = []
+    if pos < len(name) and name[pos] == "I":
+        body = name[pos + 1:name.find("EE", pos) + 1]
+        args = ["bf16" if t == "DF16b" else ("float" if t == "f" else t[2:-1])
+                for t in re.findall(r"DF16b|Li\d+E|f", body)]
+    return "::".join(parts) + (f"<{', '.join(args)}>" if args else "")
 
-    ``device_out`` holds the timed step's outputs for sample 0 (O, LSE and, for backward
-    workloads, dQ, dK, dV); each head the oracle finishes is compared with them, and the
-    largest absolute error per tensor is reported beside the largest reference value."""
+
+def trace_summary(csv_path: str, last: int) -> str:
+    """Markdown table of per-kernel durations from a rocprofv3 kernel_trace.csv: count and
+    mean over every dispatch, and mean, min and max over each kernel's last ``last``
+    dispatches (the timed steps of a run whose timed steps come last)."""
+    import csv
+    durs: dict = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = _demangle(r["Kernel_Name"]).replace("(anonymous namespace)::", "").replace("void ", "")
+            short = name.split("(")[0].strip()
+            durs.setdefault(short, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    lines = ["| kernel | calls | avg us (all) | avg us (last %d) | min us (last) | max us (last) |" % last,
+             "|---|---|---|---|---|---|"]
+    rows = []
+    for nm, v in durs.items():
+        v.sort()
+        d = np.array([(e - b) / 1e3 for b, e in v])
+        tail = d[-last:] if last > 0 else d
+        rows.append((float(d.sum()), f"| {nm} | {len(d)} | {d.mean():.1f} | {tail.mean():.1f} | {tail.min():.1f} | "
+                                     f"{tail.max():.1f} |"))
+    for _, line in sorted(rows, reverse=True):
+        lines.append(line)
+    return "\n".join(lines)
+
+
+def _oracle_head(task):
+    """One (sample, head) of the oracle, in a worker process with one BLAS thread:
+    forward (and backward) of that head over its class's block mask.  Returns the
+    outputs and the seconds it took."""
+    from threadpoolctl import threadpool_limits
+
     import oracle
+    block, cls, bm, backward, q, k, v, do = task
+    nh = [0, 0, 0]
+    nh[cls] = 1
+    sub = np.zeros((1, 3) + bm.shape, dtype=bool)
+    sub[0, cls] = bm
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        refs = list(oracle.attn_fwd(q[None, None], k[None, None], v[None, None], sub, tuple(nh), block))
+        if backward:
+            refs += list(oracle.attn_bwd(q[None, None], k[None, None], v[None, None], do[None, None], sub,
+                                         tuple(nh), block))
+        secs = time.perf_counter() - t0
+    return [r[0, 0] for r in refs], secs
+
+
+def _noop(_):
+    return os.getpid()
+
+
+def host_cores() -> int:
+    """CPUs this process may run on, capped at 16 (a GPU's share of its host)."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(wl, x_bytes, tensors, device_out, budget_s: float, workers: int | None = None):
+    """The fp64 oracle on whole (sample, head) pairs, one pair per worker process at a time
+    (one BLAS thread each), samples and heads in order: a first wave of one pair per
+    worker, then as many more pairs as the time of that wave says will fit in
+    ``budget_s`` seconds (up to the whole batch).
+
+    The oracle's gzip and mask stage for the samples taken is timed on its own.  ``value``
+    is the algorithmic FLOPs of the pairs done over the wall-clock of the attention stage.
+    ``device_out`` holds the timed step's outputs (O, LSE and, for backward workloads,
+    dQ, dK, dV) indexed [s][h] (any float dtype, on the host); each pair is compared with
+    them and the largest absolute error per tensor is reported beside the largest
+    reference value."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    import oracle
+    workers = host_cores() if workers is None else workers
+    pairs = [(s, h) for s in range(wl.batch) for h in range(wl.heads)]
     t0 = time.perf_counter()
-    c = oracle.compressed_lengths(x_bytes[:1], wl.block)
+    c = oracle.compressed_lengths(x_bytes, wl.block)
     flags, _ = oracle.literal_flags(c, wl.block)
     bm = oracle.block_masks(flags, wl.window)
     t_mask = time.perf_counter() - t0
     classes = oracle.head_classes(wl.n_heads)
     f64 = lambda z: z.float().numpy().astype(np.float64)
-    done, flops, t_attn = 0, 0.0, 0.0
-    tile = wl.block * wl.block * wl.head_dim
     names = ("o", "lse", "dq", "dk", "dv") if wl.backward else ("o", "lse")
+
+    def task(s, h):
+        hv = [f64(tensors[nm][s, h]) for nm in ("q", "k", "v")]
+        do = f64(tensors["do"][s, h]) if wl.backward else None
+        return (wl.block, classes[h], bm[s, classes[h]], wl.backward, *hv, do)
+
+    ctx = mp.get_context("spawn")
+    first = pairs[:workers]
+    with ProcessPoolExecutor(min(workers, len(pairs)), mp_context=ctx) as ex:
+        list(ex.map(_noop, range(len(first))))           # start-up outside the timed region
+        t1 = time.perf_counter()
+        results = list(ex.map(_oracle_head, [task(s, h) for s, h in first]))
+        t_wave = time.perf_counter() - t1
+        waves = int(max(0.0, budget_s - t_wave - t_mask) // max(t_wave, 1e-3))
+        more = pairs[len(first):len(first) + waves * len(first)]
+        t_more = 0.0
+        if more:
+            t1 = time.perf_counter()
+            results += list(ex.map(_oracle_head, [task(s, h) for s, h in more]))
+            t_more = time.perf_counter() - t1
+    done = first + more
+    t_attn = t_wave + t_more
+    samples = sorted({s for s, _ in done})
+    tile = wl.block * wl.block * wl.head_dim
+    flops = sum((14 if wl.backward else 4) * tile * int(bm[s, classes[h]].sum()) for s, h in done)
     err = {nm: 0.0 for nm in names}
     ref_max = {nm: 0.0 for nm in names}
-    for h in range(wl.heads):
-        q, k, v = (f64(tensors[nm][0:1, h:h + 1]) for nm in ("q", "k", "v"))
-        nh = [0, 0, 0]
-        nh[classes[h]] = 1
-        sub = np.zeros((1, 3) + bm.shape[2:], dtype=bool)
-        sub[0, classes[h]] = bm[0, classes[h]]
-        t1 = time.perf_counter()
-        refs = list(oracle.attn_fwd(q, k, v, sub, tuple(nh), wl.block))
-        if wl.backward:
-            do = f64(tensors["do"][0:1, h:h + 1])
-            refs += list(oracle.attn_bwd(q, k, v, do, sub, tuple(nh), wl.block))
-        t_attn += time.perf_counter() - t1
-        if device_out is not None:
+    if device_out is not None:
+        for (s, h), (refs, _) in zip(done, results):
             for nm, ref in zip(names, refs):
-                got = device_out[nm][h].double().numpy()
-                err[nm] = max(err[nm], float(np.max(np.abs(got - ref[0, 0]))))
+                got = device_out[nm][s][h].double().numpy()
+                err[nm] = max(err[nm], float(np.max(np.abs(got - ref))))
                 ref_max[nm] = max(ref_max[nm], float(np.max(np.abs(ref))))
-        flops += (14 if wl.backward else 4) * tile * int(bm[0, classes[h]].sum())
-        done += 1
-        if t_attn + t_mask >= budget_s:
-            break
-    secs = t_attn + t_mask
-    rec = {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-           "sample": f"sample 0 of {wl.batch}, {done} of {wl.heads} heads, full {wl.seq_len}-byte context; "
-                     f"zlib+mask {t_mask:.2f} s, attention fwd{'+bwd' if wl.backward else ''} {t_attn:.2f} s",
-           "seconds": secs}
+    per_pair = [r[1] for r in results]
+    rec = {"value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": min(workers, len(pairs)), "kind": "oracle",
+           "sample": f"{len(done)} of {len(pairs)} (sample, head) pairs (samples {samples[0]}-{samples[-1]}), full "
+                     f"{wl.seq_len}-byte context, {min(workers, len(pairs))} worker processes with one BLAS thread "
+                     f"each; zlib+mask {t_mask:.2f} s, attention fwd{'+bwd' if wl.backward else ''} {t_attn:.2f} s "
+                     f"wall (per pair {min(per_pair):.2f}-{max(per_pair):.2f} s)",
+           "seconds": t_mask + t_attn, "attention_seconds": t_attn, "mask_seconds": t_mask,
+           "pairs": len(done), "budget_s": budget_s}
     if device_out is not None:
         # the tolerances of the parity tests: absolute, on values of order one
         tol = {nm: (1e-5 if wl.dtype == "f32" else (1e-3 if nm == "lse" else 2e-2)) for nm in names}
-        rec["parity"] = {"heads": done, "tensors": {nm: {"max_abs_err": err[nm], "max_abs_ref": ref_max[nm],
-                                                          "tol": tol[nm]} for nm in names},
+        rec["parity"] = {"heads": len(done), "tensors": {nm: {"max_abs_err": err[nm], "max_abs_ref": ref_max[nm],
+                                                              "tol": tol[nm]} for nm in names},
                          "within_tol": all(err[nm] <= tol[nm] for nm in names)}
     return rec
 
@@ -282,6 +392,34 @@ class DevicePath:
             done += 10
         return spent
 
+    def time_cold(self, steps: int, warmup: int, settle_ms: float, flush):
+        """Cold-cache steps: ``flush`` (a callable that writes more than the Infinity Cache
+        holds) runs before every step, outside the events around it.  ``settle_ms`` of device
+        time in such steps and ``warmup`` more run untimed first.  Returns (median ms per
+        step, mean ms per step, mean ms per kernel, per-step ms list)."""
+        torch = self.torch
+        spent, done = 0.0, 0
+        while spent < settle_ms and done < 4000:
+            ev = self.events()
+            flush()
+            self.step(ev)
+            ev[-1].synchronize()
+            spent += ev[0].elapsed_time(ev[-1])
+            done += 1
+        for _ in range(warmup):
+            flush()
+            self.step()
+        torch.cuda.synchronize()
+        evs = [self.events() for _ in range(steps)]
+        for k in range(steps):
+            flush()
+            self.step(evs[k])
+        torch.cuda.synchronize()
+        per = {nm: [ev[i].elapsed_time(ev[i + 1]) for ev in evs] for i, nm in enumerate(self.kernels)}
+        step_ms = [ev[0].elapsed_time(ev[-1]) for ev in evs]
+        return (float(np.median(step_ms)), float(np.mean(step_ms)), {nm: float(np.mean(v)) for nm, v in per.items()},
+                step_ms)
+
     def time(self, steps: int, warmup: int, settle_ms: float = 0.0):
         """(ms per step over `steps` back-to-back steps, mean ms per kernel).
 
@@ -308,14 +446,76 @@ class DevicePath:
         return start.elapsed_time(end) / steps, {nm: float(np.mean(v)) for nm, v in per.items()}
 
 
+def roofline(wl, kern_ms: dict, tiles: int) -> dict:
+    """Roofline record of the kernel that takes the most time per step (mask kernels
+    aside): its algorithmic bytes or flops per launch over its mean launch time, against
+    the MI355X roof that binds it (HBM when its bytes take longer at peak than its flops)."""
+    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+    dom = max((nm for nm in kern_ms if nm != "mask"), key=lambda nm: kern_ms[nm])
+    nbytes, nflops = kernel_work(dom, wl, tiles)
+    t_hbm, t_mfma = nbytes / (PEAK_HBM_GBS * 1e9), nflops / (peak * 1e12)
+    sec = kern_ms[dom] * 1e-3
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(nflops / sec / 1e12, 2), "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = load_traffic(dom, wl)
+    roof["kernel"] = dom
+    roof["kernel_ms"] = round(kern_ms[dom], 4)
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = nflops
+    return roof
+
+
+def kernel_table(wl, kern_ms: dict, tiles: int) -> dict:
+    out = {}
+    for nm, ms in kern_ms.items():
+        nbytes, nflops = kernel_work(nm, wl, tiles)
+        out[nm] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                   "TFLOP/s": round(nflops / (ms * 1e-3) / 1e12, 2), "bytes": nbytes, "flops": nflops}
+    return out
+
+
+def workload_name(wl) -> str:
+    return (f"{wl.batch} x {wl.seq_len} bytes, block {wl.block}, window {wl.window}, "
+            f"{wl.heads} heads {'/'.join(map(str, wl.n_heads))}, head_dim {wl.head_dim}, "
+            f"{wl.dtype}, {'fwd+bwd' if wl.backward else 'fwd'}")
+
+
+def measure(torch, gsa, wl, dev, c, t, flush, steps: int, warmup: int, settle_ms: float, warm_steps: int = 0):
+    """Cold steps (primary) and ``warm_steps`` back-to-back steps of one workload:
+    (DevicePath, record).  The record holds the step times, per-kernel times, effective
+    TFLOP/s and the dominant kernel's roofline, all from the cold steps."""
+    path = DevicePath(torch, gsa, wl, c, t, dev)
+    med, mean, kern, step_ms = path.time_cold(steps, warmup, settle_ms, flush)
+    n_edges = path.mask.n_edges.cpu().numpy().reshape(wl.batch, 3)
+    tiles = kept_tiles(n_edges, wl.n_heads)
+    tok = token_edges(n_edges, wl.n_heads, wl.n_blocks, wl.block)
+    fl = (4 + (10 if wl.backward else 0)) * wl.block * wl.block * wl.head_dim
+    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+    value = fl * tiles / (med * 1e-3) / 1e12
+    rec = {"workload": workload_name(wl), "dtype": wl.dtype, "steps": steps, "ms_per_step": round(med, 4),
+           "ms_per_step_mean": round(mean, 4), "ms_per_step_min": round(min(step_ms), 4),
+           "tflops": round(value, 3), "pct_mfma_peak": round(100 * value / peak, 2),
+           "token_exact_tflops": round((fl // (wl.block * wl.block)) * tok / (med * 1e-3) / 1e12, 3),
+           "kept_tiles": tiles, "literal_blocks": path.mask.n_literal.cpu().numpy()[:wl.batch].tolist(),
+           "kernels": kernel_table(wl, kern, tiles), "roofline": roofline(wl, kern, tiles)}
+    if warm_steps > 0:
+        w_ms, w_kern = path.time(warm_steps, warmup, 0.0)
+        rec["warm"] = {"ms_per_step": round(w_ms, 4), "tflops": round(fl * tiles / (w_ms * 1e-3) / 1e12, 3),
+                       "kernels_ms": {nm: round(v, 4) for nm, v in w_kern.items()}}
+    return path, rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50, help="timed cold steps (median reported)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-ms", type=float, default=40.0,
-                    help="untimed device time before the warm-up steps: the first ~25 ms of sustained "
-                         "load run up to 20%% slower while the clocks settle (0: none)")
+                    help="untimed device time (in cold steps) before the warm-up steps: the first ~25 ms "
+                         "of sustained load run up to 20%% slower while the clocks settle (0: none)")
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5); 4 is the headline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0: skip)")
     ap.add_argument("--dense", action="store_true",
@@ -328,14 +528,23 @@ def main():
                     help="fwd+bwd steps of the ByteLM attention layer (projections + kernels) (0: skip)")
     ap.add_argument("--pipeline-steps", type=int, default=20,
                     help="batches for the serial vs pipelined host-stage comparison (0: skip)")
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="extra steps timed one by one after a 512 MiB cache flush (0: skip)")
+    ap.add_argument("--other-configs", default="1,2,3,5",
+                    help="comma-separated workload ids also timed (cold protocol, --other-steps steps)")
+    ap.add_argument("--other-steps", type=int, default=20)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain elementwise copy of this many MiB 3 times (HBM counter calibration)")
+    ap.add_argument("--warm-steps", type=int, default=-1,
+                    help="back-to-back (warm) steps timed after the cold ones (-1: as many as --steps; 0: none)")
+    ap.add_argument("--trace-from", metavar="KERNEL_TRACE_CSV",
+                    help="no GPU: per-kernel durations of a rocprofv3 kernel_trace.csv, over every dispatch "
+                         "and over each kernel's last --steps dispatches")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then "
                          "WRITE_SIZE, of a run with --copy-mib) into per-launch HBM bytes under profiles/")
     args = ap.parse_args()
+    if args.trace_from:
+        print(trace_summary(args.trace_from, args.steps))
+        return
     if args.traffic_from:
         record_traffic(args, *args.traffic_from)
         return
@@ -381,14 +590,21 @@ def main():
         gsa.gsa_prepare(x, wl.block, n_threads=1)
     prep1_ms = (time.perf_counter() - t0) / 3 * 1e3
 
-    path = DevicePath(torch, gsa, wl, c, t, dev)
-    ms_step, kern_ms = path.time(args.steps, args.warmup, args.settle_ms)
+    flush_buf = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+
+    def flush():
+        flush_buf.fill_(1.0)
+
+    warm_steps = args.steps if args.warm_steps < 0 else args.warm_steps
+    path, head = measure(torch, gsa, wl, dev, c, t, flush, args.steps, args.warmup, args.settle_ms, warm_steps)
+    ms_step = head["ms_per_step"]
+    kern_ms = {nm: v["ms"] for nm, v in head["kernels"].items()}
     mask = path.mask
-    # The timed steps' outputs for sample 0, for the oracle comparison in cpu_baseline.
+    # The timed steps' outputs (host copies), for the oracle comparison in cpu_baseline.
     device_out = None
     if args.cpu_budget > 0:
         outs = (path.o, path.lse) + (path.grads if wl.backward else ())
-        device_out = {nm: x_[0].float().cpu() for nm, x_ in zip(("o", "lse", "dq", "dk", "dv"), outs)}
+        device_out = {nm: x_.cpu() for nm, x_ in zip(("o", "lse", "dq", "dk", "dv"), outs)}
     # The hand-over of c from pinned host memory (4 bytes per block over PCIe), timed on
     # its own: the step starts from c resident in HBM.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -398,24 +614,6 @@ def main():
     e1.record(path.stream)
     torch.cuda.synchronize()
     upload_ms = e0.elapsed_time(e1) / 50
-
-    # Cold-cache steps: a 512 MiB write (more than the 256 MB MALL) before each step,
-    # outside the events that time it.
-    cold = None
-    if args.cold_steps > 0:
-        flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
-        cold_ms = []
-        for _ in range(args.cold_steps):
-            flush.fill_(1.0)
-            ev = path.events()
-            path.step(ev)
-            torch.cuda.synchronize()
-            cold_ms.append([ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)])
-        del flush
-        cold_arr = np.array(cold_ms)
-        cold = {"steps": args.cold_steps, "ms_per_step": round(float(np.median(cold_arr.sum(axis=1))), 4),
-                "kernels_ms": {nm: round(float(np.median(cold_arr[:, i])), 4)
-                               for i, nm in enumerate(path.kernels)}}
 
     # Host-stage pipeline: the gzip sizes of batch k + 1 are computed by the persistent
     # pool while the device runs batch k (MaskPipeline), against the serial order (sizes,
@@ -447,7 +645,8 @@ def main():
         path.c_dev.copy_(path.c_host)
         torch.cuda.synchronize()
         pipeline = {"batches": k_steps, "host_threads": threads, "serial_ms_per_batch": round(serial, 4),
-                    "pipelined_ms_per_batch": round(pipelined, 4), "device_ms_per_step": round(ms_step, 4)}
+                    "pipelined_ms_per_batch": round(pipelined, 4),
+                    "device_ms_per_step_warm": head["warm"]["ms_per_step"] if head.get("warm") else None}
 
     # ByteLM attention layer at this shape: Q/K/V and output projections (D = H d) around
     # the same kernels, forward and backward.
@@ -473,7 +672,8 @@ def main():
         e1.record(path.stream)
         torch.cuda.synchronize()
         l_ms = e0.elapsed_time(e1) / args.layer_steps
-        attn_ms = kern_ms["fwd"] + kern_ms.get("bwd_dq", 0.0) + kern_ms.get("bwd_dkdv", 0.0)
+        wk = head["warm"]["kernels_ms"] if head.get("warm") else kern_ms   # back-to-back, like the layer
+        attn_ms = wk["fwd"] + wk.get("bwd_dq", 0.0) + wk.get("bwd_dkdv", 0.0)
         layer = {"d_model": dm, "ms_fwd_bwd": round(l_ms, 4), "attention_ms": round(attn_ms, 4),
                  "attention_share": round(attn_ms / l_ms, 3)}
         del lyr, xin, gy
@@ -488,7 +688,7 @@ def main():
         blocks = gsa.gsa_bigbird_blocks(torch.from_numpy(picks).to(dev), wl.window, n_global)
         bwl = dataclasses.replace(wl, name=wl.name + "-bigbird", n_heads=(wl.heads, 0, 0))
         bpath = DevicePath(torch, gsa, bwl, c, t, dev, blocks=blocks)
-        b_ms, b_kern = bpath.time(args.bigbird_steps, 2)
+        b_ms, _, b_kern, _ = bpath.time_cold(args.bigbird_steps, 2, 0.0, flush)
         b_edges = bpath.mask.n_edges.cpu().numpy().reshape(wl.batch, 3)
         b_tiles = kept_tiles(b_edges, bwl.n_heads)
         b_flops = (4 + (10 if wl.backward else 0)) * wl.block * wl.block * wl.head_dim * b_tiles
@@ -496,7 +696,7 @@ def main():
         g_attn = sum(v for nm, v in kern_ms.items() if nm != "mask")
         bigbird = {"window": wl.window, "n_global": n_global, "n_random": n_random, "kept_tiles": b_tiles,
                    "gzip_kept_tiles": kept_tiles(path.mask.n_edges.cpu().numpy().reshape(wl.batch, 3), wl.n_heads),
-                   "mask": "fixed: lists built once, outside the timed steps",
+                   "mask": "fixed: lists built once, outside the timed (cold) steps",
                    "ms_per_step": round(b_ms, 4), "kernels_ms": {nm: round(v, 4) for nm, v in b_kern.items()},
                    "attention_ms": round(b_attn, 4), "gzip_attention_ms": round(g_attn, 4),
                    "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 3)}
@@ -508,59 +708,28 @@ def main():
     if args.dense_steps > 0 and wl.window < wl.n_blocks - 1:
         dwl = synth.dense_causal(wl)
         dpath = DevicePath(torch, gsa, dwl, c, t, dev)
-        d_ms, d_kern = dpath.time(args.dense_steps, 2)
+        d_ms, _, d_kern, _ = dpath.time_cold(args.dense_steps, 1, 0.0, flush)
         dense = {"workload": dwl.name, "ms_per_step": round(d_ms, 4),
                  "kernels_ms": {nm: round(v, 4) for nm, v in d_kern.items()},
                  "sparse_speedup": round(d_ms / ms_step, 2)}
         del dpath
 
     n_edges = mask.n_edges.cpu().numpy().reshape(wl.batch, 3)
-    n_lit = mask.n_literal.cpu().numpy()[:wl.batch]
-    tiles = kept_tiles(n_edges, wl.n_heads)
-    tok = token_edges(n_edges, wl.n_heads, wl.n_blocks, wl.block)
-    tile = wl.block * wl.block * wl.head_dim
-    fl_fwd, fl_bwd = 4 * tile * tiles, (10 * tile * tiles if wl.backward else 0)
-    flops = fl_fwd + fl_bwd
-    value = flops / (ms_step * 1e-3) / 1e12
-    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
-    fwd_ms = kern_ms["fwd"]
-    bwd_ms = sum(kern_ms.get(nm, 0.0) for nm in ("bwd_dq", "bwd_dkdv"))
-
-    kernels = {}
-    for nm, ms in kern_ms.items():
-        nbytes, nflops = kernel_work(nm, wl, tiles)
-        kernels[nm] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                       "TFLOP/s": round(nflops / (ms * 1e-3) / 1e12, 2), "bytes": nbytes, "flops": nflops}
-    dom = max((nm for nm in kern_ms if nm != "mask"), key=lambda nm: kern_ms[nm])
-    nbytes, nflops = kernel_work(dom, wl, tiles)
-    t_hbm, t_mfma = nbytes / (PEAK_HBM_GBS * 1e9), nflops / (peak * 1e12)
-    sec = kern_ms[dom] * 1e-3
-    traffic = load_traffic(dom, wl)
-    if t_hbm >= t_mfma:
-        roof = {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": round(nflops / sec / 1e12, 2), "peak": peak, "unit": "TFLOP/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = traffic
-    roof["kernel"] = dom
-    roof["algorithmic_bytes"] = nbytes
-    roof["algorithmic_flops"] = nflops
-
     rec = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": f"{wl.batch} x {wl.seq_len} bytes, block {wl.block}, window {wl.window}, "
-                               f"{wl.heads} heads {'/'.join(map(str, wl.n_heads))}, head_dim {wl.head_dim}, "
-                               f"{wl.dtype}, {'fwd+bwd' if wl.backward else 'fwd'}",
-                   "global_batch": wl.batch, "seq_len": wl.seq_len, "parallelism": "single GPU"},
-        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "mask_ms": round(kern_ms["mask"], 4),
+        "metric": METRIC, "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": head["workload"], "global_batch": wl.batch, "seq_len": wl.seq_len,
+                   "parallelism": "single GPU"},
+        "timing": "cold: 512 MiB written before every step, outside its events; median of the timed steps",
+        "ms_per_step_mean": head["ms_per_step_mean"], "ms_per_step_min": head["ms_per_step_min"],
+        "fwd_ms": round(kern_ms["fwd"], 4), "bwd_ms": round(sum(kern_ms.get(nm, 0.0) for nm in ("bwd_dq", "bwd_dkdv")), 4),
+        "mask_ms": round(kern_ms["mask"], 4),
         "c_upload_ms": round(upload_ms, 4), "ms_per_step_with_upload": round(ms_step + upload_ms, 4),
-        "pct_mfma_peak": round(100 * value / peak, 2),
-        "token_exact_tflops": round((4 + (10 if wl.backward else 0)) * wl.head_dim * tok / (ms_step * 1e-3) / 1e12, 3),
-        "kept_tiles": tiles, "literal_blocks": n_lit.tolist(),
+        "pct_mfma_peak": head["pct_mfma_peak"], "token_exact_tflops": head["token_exact_tflops"],
+        "kept_tiles": head["kept_tiles"], "literal_blocks": head["literal_blocks"],
         "host_prepare_ms": {"all_cores": round(prep_ms, 3), "one_thread": round(prep1_ms, 3)},
-        "kernels": kernels, "roofline": roof, "cold": cold, "dense_causal": dense,
+        "kernels": head["kernels"], "roofline": head["roofline"], "warm": head.get("warm"), "dense_causal": dense,
         "host_pipeline": pipeline, "layer": layer, "bigbird": bigbird,
         "n_edges": n_edges.tolist(),
         "env": {"gpu": torch.cuda.get_device_name(dev), "hip": torch.version.hip, "torch": torch.__version__,
@@ -571,6 +740,27 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(wl, x, host_t, device_out, args.cpu_budget)
     else:
         rec["cpu_baseline"] = None
+    del path, t, device_out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # The other workloads: the same cold protocol with fewer steps, no oracle.
+    others = {}
+    for cid in [int(z) for z in args.other_configs.split(",") if z.strip()]:
+        if cid == args.config or cid not in synth.WORKLOADS:
+            continue
+        owl = synth.WORKLOADS[cid]
+        onames = ("q", "k", "v", "do") if owl.backward else ("q", "k", "v")
+        ox = synth.gen_bytes(owl)
+        ot = {nm: v.to(dev) for nm, v in synth.gen_tensors(owl, onames).items()}
+        oc = gsa.gsa_prepare(ox, owl.block)
+        opath, orec = measure(torch, gsa, owl, dev, oc, ot, flush, args.other_steps, 3, args.settle_ms / 2,
+                              args.other_steps)
+        others[str(cid)] = orec
+        del opath, ot
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    rec["configs"] = others
     print(json.dumps(rec), flush=True)
 
 

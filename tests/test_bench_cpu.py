@@ -102,11 +102,37 @@ def test_cpu_baseline_reports_parity_against_the_device_outputs():
     bm = oracle.block_masks(flags, wl.window)
     f64 = lambda z: z.double().numpy()
     o, lse = oracle.attn_fwd(f64(t["q"][:1]), f64(t["k"][:1]), f64(t["v"][:1]), bm, wl.n_heads, wl.block)
-    dev = {"o": torch.from_numpy(o[0]).float(), "lse": torch.from_numpy(lse[0]).float()}
+    dev = {"o": torch.from_numpy(o).float(), "lse": torch.from_numpy(lse).float()}   # [s][h]
     rec = bench.cpu_baseline(wl, x, t, dev, budget_s=60.0)
+    assert rec["cores"] == wl.heads and rec["value"] > 0
     par = rec["parity"]
     assert par["heads"] == wl.heads and par["within_tol"]
     assert par["tensors"]["o"]["max_abs_err"] < 1e-6 and par["tensors"]["o"]["max_abs_ref"] > 0.1
     dev["o"] = dev["o"] + 1e-3
     par = bench.cpu_baseline(wl, x, t, dev, budget_s=60.0)["parity"]
     assert not par["within_tol"] and abs(par["tensors"]["o"]["max_abs_err"] - 1e-3) < 1e-6
+
+
+def test_trace_summary_takes_the_last_dispatches(tmp_path):
+    # two dispatches of one kernel (1 us, then 2 us) and one of another: the "last 1"
+    # column holds the second dispatch only
+    p = tmp_path / "kernel_trace.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerow({"Kernel_Name": "void gsa::attn_fwd_kernel<bf16>(int)", "Start_Timestamp": 100,
+                    "End_Timestamp": 1100})
+        w.writerow({"Kernel_Name": "void gsa::attn_fwd_kernel<bf16>(int)", "Start_Timestamp": 2000,
+                    "End_Timestamp": 4000})
+        w.writerow({"Kernel_Name": "mask_kernel(int)", "Start_Timestamp": 10, "End_Timestamp": 510})
+    out = bench.trace_summary(str(p), 1)
+    row = [l for l in out.splitlines() if "attn_fwd_kernel" in l][0]
+    assert [c.strip() for c in row.split("|")[2:7]] == ["2", "1.5", "2.0", "2.0", "2.0"]
+
+
+def test_demangle_kernel_names():
+    assert bench._demangle("_ZN3gsa12_GLOBAL__N_115attn_fwd_kernelIDF16bLi64ELi64EEEvPKT_S4_S4_PS2_PfNS_9WorkListsEf") \
+        == "gsa::attn_fwd_kernel<bf16, 64, 64>"
+    assert bench._demangle("_ZN3gsa12_GLOBAL__N_115bwd_dkdv_kernelIfLi16ELi32EEEvPKT_S4_S4_S4_PKfS6_PS2_S7_NS_9WorkLi"
+                           "stsEff") == "gsa::bwd_dkdv_kernel<float, 16, 32>"
+    assert bench._demangle("gsa::mask_kernel(int)") == "gsa::mask_kernel(int)"
