@@ -16,7 +16,8 @@
 //             one piece ahead (32-row pieces at b = 64, whole blocks otherwise); Q_i^T
 //             and dO_i^T come from transposing LDS reads.
 //   bwd_dq    one workgroup per (sample, head, query block i), walking the CSR row of i;
-//             each wave keeps 16 query rows of Q_i and dO_i in registers and accumulates
+//             each wave keeps 16 query rows (32 at b = d = 128) of Q_i and dO_i in
+//             registers and accumulates
 //             dQ^T while K_j and V_j stream through a ring of three LDS slots (V's slot
 //             takes the next V as soon as dS is formed; K^T by transposing reads); at
 //             b = 128, d = 128 the blocks stream as 64-row pieces.
@@ -66,9 +67,23 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ o, c
 #ifndef GSA_DKDV_GROUPS
 #define GSA_DKDV_GROUPS 2
 #endif
+// At b = d = 128 (the _WIDE options): one 16-key group per wave, whole query blocks, one
+// 8-wave workgroup per CU.  Two groups need 128 VGPRs of accumulators alone and spill
+// (176-352 bytes per lane) at the two waves per SIMD that 64-row query pieces would allow.
+#ifndef GSA_DKDV_GROUPS_WIDE
+#define GSA_DKDV_GROUPS_WIDE 1
+#endif
+#ifndef GSA_DKDV_PIECE_WIDE
+#define GSA_DKDV_PIECE_WIDE 128
+#endif
+#ifndef GSA_DKDV_WAVES_WIDE
+#define GSA_DKDV_WAVES_WIDE 1
+#endif
 template <typename T, int BLK, int HD>
 constexpr int dkdv_groups() {
-  return std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0 ? GSA_DKDV_GROUPS : 1;
+  if (std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0) return GSA_DKDV_GROUPS;
+  if (std::is_same<T, bf16_t>::value && HD == 128 && BLK == 128) return GSA_DKDV_GROUPS_WIDE;
+  return 1;
 }
 
 // Query rows per streamed piece of dK/dV (GSA_DKDV_PIECE at b = 64, d = 64, bf16).  With
@@ -81,7 +96,9 @@ constexpr int dkdv_groups() {
 #endif
 template <typename T, int BLK, int HD>
 constexpr int dkdv_piece_rows() {
-  return std::is_same<T, bf16_t>::value && BLK == 64 && HD == 64 ? GSA_DKDV_PIECE : BLK;
+  if (std::is_same<T, bf16_t>::value && BLK == 64 && HD == 64) return GSA_DKDV_PIECE;
+  if (std::is_same<T, bf16_t>::value && BLK == 128 && HD == 128) return GSA_DKDV_PIECE_WIDE;
+  return BLK;
 }
 
 // dK, dV of one (sample, head, kv-block j): walk the query blocks i of column j.  Each
@@ -207,7 +224,7 @@ struct DkdvPolicy {
 
 template <typename T, int BLK, int HD>
 __global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64),
-                             (dkdv_piece_rows<T, BLK, HD>() < BLK ? 3 : 1)) void bwd_dkdv_kernel(
+                             (HD == 128 ? GSA_DKDV_WAVES_WIDE : (dkdv_piece_rows<T, BLK, HD>() < BLK ? 3 : 1))) void bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ dvec, T *__restrict__ dk, T *__restrict__ dv,
     WorkLists wl, float sl2, float scale) {
@@ -236,12 +253,25 @@ __global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64),
   run_item(pol, it);
 }
 
+// 16-row query groups per wave in dQ.  At b = d = 128 eight one-group waves read 768 KiB
+// of LDS per kept tile (K twice, V once), over 100 bytes per clock per CU; with two groups
+// every K and V read feeds two products (4 waves, 235 VGPRs, two waves per SIMD):
+// 3.19-3.20 vs 3.40-3.42 ms at 2 x 64 KiB.  At b = d = 64 two groups measured no faster.
+#ifndef GSA_DQ_GROUPS_WIDE
+#define GSA_DQ_GROUPS_WIDE 2
+#endif
+template <typename T, int BLK, int HD>
+constexpr int dq_groups() {
+  return std::is_same<T, bf16_t>::value && BLK == 128 && HD == 128 ? GSA_DQ_GROUPS_WIDE : 1;
+}
+
 // dQ of one (sample, head, query block i): walk the kv-blocks j of row i.  The item's
 // D = rowsum(dO * O) is formed from the rows it loads anyway and written out for dK/dV.
-template <typename T, int BLK, int HD>
+// Each wave owns R groups of 16 query rows.
+template <typename T, int BLK, int HD, int R>
 struct DqPolicy {
   static constexpr int KC = kv_piece_rows<T, BLK, HD>();
-  using S = AttnShape<T, BLK, HD, 1, KC>;
+  using S = AttnShape<T, BLK, HD, R, KC>;
   using Item = WorkItem;
   static constexpr int kSub = BLK / KC;                  // pieces per kv-block
   static constexpr int kLdsBytes = 3 * S::kTileBytes;   // the ring: K, V and a spare
@@ -253,36 +283,41 @@ struct DqPolicy {
   int64_t seq;
   float sl2, scale;
   unsigned char *lds;
-  int tid, c, g, q_in_blk;
+  int tid, c, g, q_in_blk;   // q_in_blk: this lane's query of group 0; group r: + 16 r
 
-  typename S::QFrag qf, dof;
-  float lse2, dd;
-  f32x4 acc[S::kDB];
+  typename S::QFrag qf[R], dof[R];
+  float lse2[R], dd[R];
+  f32x4 acc[R][S::kDB];
 
   __device__ void operands(const Item &it) {
-    const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk;
-    typename S::QFrag of;
-    S::load_row_frag(qf, q + q_row * HD, g);
-    S::load_row_frag(dof, dout + q_row * HD, g);
-    S::load_row_frag(of, o + q_row * HD, g);
-    lse2 = lse[q_row] * kLog2e;
-    // D over this lane's feature slots, then across the four lane groups of the row.
-    float part = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < S::kKS; ++ks) {
-      if constexpr (S::kBf16) {
+    for (int r = 0; r < R; ++r) {
+      const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk + 16 * r;
+      typename S::QFrag of;
+      S::load_row_frag(qf[r], q + q_row * HD, g);
+      S::load_row_frag(dof[r], dout + q_row * HD, g);
+      S::load_row_frag(of, o + q_row * HD, g);
+      lse2[r] = lse[q_row] * kLog2e;
+      // D over this lane's feature slots, then across the four lane groups of the row.
+      float part = 0.f;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) part = fmaf(to_f32(dof.f[ks][x]), to_f32(of.f[ks][x]), part);
-      } else {
-        part = fmaf(dof.f[ks], of.f[ks], part);
+      for (int ks = 0; ks < S::kKS; ++ks) {
+        if constexpr (S::kBf16) {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) part = fmaf(to_f32(dof[r].f[ks][x]), to_f32(of.f[ks][x]), part);
+        } else {
+          part = fmaf(dof[r].f[ks], of.f[ks], part);
+        }
       }
+      dd[r] = group_sum4(part);
+      if (g == 0) dvec[q_row] = dd[r];
     }
-    dd = group_sum4(part);
-    if (g == 0) dvec[q_row] = dd;
   }
   __device__ void begin(const Item &) {
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db) acc[r][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   static constexpr bool kFreeK = false;   // V_j is done once dS is formed; K_j is read again
   __device__ void copy_k(const Item &it, int j, int piece, int slot) {
@@ -292,22 +327,41 @@ struct DqPolicy {
     S::copy_tile(lds + slot * S::kTileBytes, v + (it.sh * seq + (int64_t)j * BLK + piece * KC) * HD, tid);
   }
   // dS^T[key][q] of every key of the piece (lane holds keys piece*KC + kb*16 + 4g + r of its
-  // query): S^T from K and dP^T - D from V.
-  f32x4 dsr[S::kKB];
+  // query of group rg): S^T from K and dP^T - D from V.
+  f32x4 dsr[R][S::kKB];
   __device__ void compute_a(const Item &it, int e, int piece, int k_slot, int v_slot) {
     const unsigned char *lk = lds + k_slot * S::kTileBytes;
     const unsigned char *lv = lds + v_slot * S::kTileBytes;
     const bool diag = e == it.end - 1;   // row i ends with its own block j = i
+    if constexpr (R == 1) {
 #pragma unroll
-    for (int kb = 0; kb < S::kKB; ++kb) {
-      const f32x4 st = S::dot_rows(lk, kb * 16 + c, g, qf);
-      const f32x4 dpd = S::dot_rows(lv, kb * 16 + c, g, dof, f32x4{-dd, -dd, -dd, -dd});   // dP - D
+      for (int kb = 0; kb < S::kKB; ++kb) {
+        const f32x4 st = S::dot_rows(lk, kb * 16 + c, g, qf[0]);
+        const f32x4 dpd = S::dot_rows(lv, kb * 16 + c, g, dof[0], f32x4{-dd[0], -dd[0], -dd[0], -dd[0]});   // dP - D
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dsr[kb][r] = fast_exp2(fmaf(st[r], sl2, -lse2)) * dpd[r];
-      if (diag) {   // token-causal mask, diagonal block only
+        for (int r = 0; r < 4; ++r) dsr[0][kb][r] = fast_exp2(fmaf(st[r], sl2, -lse2[0])) * dpd[r];
+        if (diag) {   // token-causal mask, diagonal block only
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (piece * KC + kb * 16 + 4 * g + r > q_in_blk) dsr[kb][r] = 0.f;
+          for (int r = 0; r < 4; ++r)
+            if (piece * KC + kb * 16 + 4 * g + r > q_in_blk) dsr[0][kb][r] = 0.f;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < S::kKB; ++kb) {
+        f32x4 st[R], dp[R];
+        S::template dot_rows_n<R>(lk, kb * 16 + c, g, qf, st);
+        S::template dot_rows_n<R>(lv, kb * 16 + c, g, dof, dp);
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dsr[rg][kb][r] = fast_exp2(fmaf(st[rg][r], sl2, -lse2[rg])) * (dp[rg][r] - dd[rg]);
+          if (diag) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (piece * KC + kb * 16 + 4 * g + r > q_in_blk + 16 * rg) dsr[rg][kb][r] = 0.f;
+          }
+        }
       }
     }
   }
@@ -316,22 +370,26 @@ struct DqPolicy {
     const unsigned char *lk = lds + k_slot * S::kTileBytes;
 #pragma unroll
     for (int part = 0; part < S::kParts; ++part)
-      S::accumulate_part(acc, lk, &dsr[part * S::kPartTiles], part, c, g);
+      S::template accumulate_part_n<R>(&acc[0][0], lk, &dsr[0][part * S::kPartTiles], S::kKB, part, c, g);
   }
   __device__ void finish(const Item &it) {
-    const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk;
-    T *dqr = dq + q_row * HD;
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) S::store4(dqr + db * 16 + 4 * g, acc[db] * scale);
+    for (int r = 0; r < R; ++r) {
+      const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk + 16 * r;
+      T *dqr = dq + q_row * HD;
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db) S::store4(dqr + db * 16 + 4 * g, acc[r][db] * scale);
+    }
   }
 };
 
 template <typename T, int BLK, int HD>
-__global__ __launch_bounds__(BLK / 16 * 64, HD <= 64 ? 1 : 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(BLK / (16 * dq_groups<T, BLK, HD>()) * 64, HD <= 64 ? 1 : 2) void bwd_dq_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ o,
     const T *__restrict__ dout, const float *__restrict__ lse, float *__restrict__ dvec, T *__restrict__ dq,
     WorkLists wl, float sl2, float scale) {
-  using P = DqPolicy<T, BLK, HD>;
+  constexpr int R = dq_groups<T, BLK, HD>();
+  using P = DqPolicy<T, BLK, HD, R>;
   __shared__ __align__(16) unsigned char lds[P::kLdsBytes];
   const WorkItem it = wl.decode(dispatch_position(blockIdx.x, gridDim.x));
 
@@ -351,13 +409,13 @@ __global__ __launch_bounds__(BLK / 16 * 64, HD <= 64 ? 1 : 2) void bwd_dq_kernel
   pol.tid = threadIdx.x;
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
-  pol.q_in_blk = (threadIdx.x >> 6) * 16 + pol.c;
+  pol.q_in_blk = (threadIdx.x >> 6) * 16 * R + pol.c;
   run_item_ring(pol, it);
 }
 
 template <typename T, int BLK, int HD>
 gsa_status launch_dq_instance(const gsa_bwd_args &a, const gsa_mask &m, hipStream_t stream) {
-  using S = AttnShape<T, BLK, HD>;
+  using S = AttnShape<T, BLK, HD, dq_groups<T, BLK, HD>()>;
   const gsa_fwd_args &f = a.f;
   const int64_t items = f.batch * f.heads * (int64_t)m.n_blocks;
   const float scale = f.scale > 0.f ? f.scale : 1.0f / sqrtf((float)HD);

@@ -7,13 +7,12 @@
 // diagonal block.  Keys outside the kept blocks carry exactly zero weight in the dense
 // masked form, so visiting only the kept blocks gives the same result.
 //
-// Design (one workgroup per (sample, head, query block); each wave owns 16 or 32 of its
-// query rows):
+// Design (one workgroup per (sample, head, query block); each wave owns 16 of its query
+// rows, 32 at b = d = 128):
 //   * The query rows of a wave stay in registers as the B operand of S^T = K Q^T, so
 //     each lane owns one query column of every score tile and its online-softmax state
 //     (running max m and a lane-partial sum l); the row max needs two permlane swaps.
-//     With two 16-row groups per wave (a build option) every K and V read from LDS feeds
-//     two products.
+//     With two 16-row groups per wave every K and V read from LDS feeds two products.
 //   * K_j and V_j stream row-major (swizzled) into a ring of three LDS tiles by
 //     asynchronous global -> LDS copies: K_{j+1} lands in the spare tile while block j
 //     is computed, V_{j+1} in K_j's tile once the scores of block j are done (at
@@ -42,12 +41,21 @@ constexpr float kMaskedScore = -1.0e30f;
 #ifndef GSA_FWD_GROUPS
 #define GSA_FWD_GROUPS 1
 #endif
-// 16-row query groups per wave (GSA_FWD_GROUPS, bf16 at head_dim 64 only).  Two groups
-// halve the LDS reads per tile but need 146 VGPRs, which halves the resident waves; on
-// gfx950 at 8 x 8 KiB that measured slower (147 vs 135 us), so one group is the default.
+// 16-row query groups per wave.  Two groups halve the LDS reads per tile (every K and V
+// read feeds two products) but need more registers.  At b = d = 64 (GSA_FWD_GROUPS) they
+// need 146 VGPRs, which halves the resident waves: 147 vs 135 us at 8 x 8 KiB, so one
+// group.  At b = d = 128 (GSA_FWD_GROUPS_WIDE) eight one-group waves read 512 KiB of LDS
+// per kept tile, about 90 bytes per clock per CU, so LDS bandwidth binds; two groups (4
+// waves, 215 VGPRs, two waves per SIMD) read half of it: 2.36-2.46 vs 2.56-2.61 ms at
+// 2 x 64 KiB.
+#ifndef GSA_FWD_GROUPS_WIDE
+#define GSA_FWD_GROUPS_WIDE 2
+#endif
 template <typename T, int BLK, int HD>
 constexpr int fwd_groups() {
-  return std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0 ? GSA_FWD_GROUPS : 1;
+  if (std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0) return GSA_FWD_GROUPS;
+  if (std::is_same<T, bf16_t>::value && HD == 128 && BLK == 128) return GSA_FWD_GROUPS_WIDE;
+  return 1;
 }
 
 template <typename T, int BLK, int HD, int R>

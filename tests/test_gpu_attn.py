@@ -267,6 +267,12 @@ def test_full_size_sampled(cid):
                 errs.setdefault("dV (columns > 64 entries)", []).append(errs["dV"][-1])
         if cid == 5:
             assert "dV (columns > 64 entries)" in errs
+        # The 2e-2 bound is absolute and bf16 outputs on [8, 16) are 2^-4 apart, so it holds
+        # only while every |dV| stays below 8: check the whole device tensor (its error
+        # against the oracle is below 2e-2 where sampled).
+        dv_max = float(res["dv"].abs().max())
+        log(f"    max|dV| over the whole tensor: {dv_max:.3f}")
+        assert dv_max < 8.0
     _compare_sampled(errs, ltol, tol)
 
 
