@@ -121,11 +121,17 @@ struct DkdvPolicy {
   float sl2, scale;
   unsigned char *lds;
   int tid, c, g, key0;   // key0: this lane's key of group 0 inside block j
+  int wave, lane;        // wave: wave-uniform
+  rsrc_t rq, rdo, rl, rd;   // Q, dO, LSE, D of the item's (sample, head)
 
   typename S::QFrag kf[R], vf[R];
   f32x4 dk_acc[R][S::kDB], dv_acc[R][S::kDB];
 
   __device__ void operands(const Item &it) {
+    rq = make_rsrc(q + it.sh * seq * HD, (uint32_t)(seq * S::kRowBytes));
+    rdo = make_rsrc(dout + it.sh * seq * HD, (uint32_t)(seq * S::kRowBytes));
+    rl = make_rsrc(lse + it.sh * seq, (uint32_t)(seq * 4));
+    rd = make_rsrc(dvec + it.sh * seq, (uint32_t)(seq * 4));
 #pragma unroll
     for (int kg = 0; kg < R; ++kg) {
       const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key0 + 16 * kg;
@@ -153,15 +159,14 @@ struct DkdvPolicy {
       }
   }
   __device__ void copy(const Item &it, int i, int piece, int stage) {
-    const int64_t row0 = it.sh * seq + (int64_t)i * BLK + piece * KQ;
     unsigned char *dst = lds + stage * kStageBytes;
-    S::copy_tile(dst, q + row0 * HD, tid);
-    S::copy_tile(dst + S::kTileBytes, dout + row0 * HD, tid);
-    const int wave = tid >> 6, lane = tid & 63;
+    const int r0 = i * BLK + piece * KQ;   // first row of the piece in the (sample, head) slice
+    S::copy_tile_buf(dst, rq, (uint32_t)(r0 * S::kRowBytes), wave, lane);
+    S::copy_tile_buf(dst + S::kTileBytes, rdo, (uint32_t)(r0 * S::kRowBytes), wave, lane);
     if (lane < kVecLanes) {
-      const int x = wave * kVecLanes + lane;
-      copy4_to_lds(lse + row0 + x, dst + 2 * S::kTileBytes + wave * kVecLanes * 4);
-      copy4_to_lds(dvec + row0 + x, dst + 2 * S::kTileBytes + KQ * 4 + wave * kVecLanes * 4);
+      const uint32_t x4 = (uint32_t)((wave * kVecLanes + lane) * 4);
+      buf_copy4_to_lds(rl, x4, (uint32_t)(r0 * 4), dst + 2 * S::kTileBytes + wave * kVecLanes * 4);
+      buf_copy4_to_lds(rd, x4, (uint32_t)(r0 * 4), dst + 2 * S::kTileBytes + KQ * 4 + wave * kVecLanes * 4);
     }
   }
   __device__ void compute(const Item &it, int e, int piece, int stage) {
@@ -247,6 +252,8 @@ __global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64),
   pol.scale = scale;
   pol.lds = lds;
   pol.tid = threadIdx.x;
+  pol.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  pol.lane = threadIdx.x & 63;
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
   pol.key0 = (threadIdx.x >> 6) * 16 * R + pol.c;
@@ -284,12 +291,16 @@ struct DqPolicy {
   float sl2, scale;
   unsigned char *lds;
   int tid, c, g, q_in_blk;   // q_in_blk: this lane's query of group 0; group r: + 16 r
+  int wave, lane;            // wave: wave-uniform
+  rsrc_t rk, rv;             // K and V of the item's (sample, head)
 
   typename S::QFrag qf[R], dof[R];
   float lse2[R], dd[R];
   f32x4 acc[R][S::kDB];
 
   __device__ void operands(const Item &it) {
+    rk = make_rsrc(k + it.sh * seq * HD, (uint32_t)(seq * S::kRowBytes));
+    rv = make_rsrc(v + it.sh * seq * HD, (uint32_t)(seq * S::kRowBytes));
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk + 16 * r;
@@ -321,10 +332,10 @@ struct DqPolicy {
   }
   static constexpr bool kFreeK = false;   // V_j is done once dS is formed; K_j is read again
   __device__ void copy_k(const Item &it, int j, int piece, int slot) {
-    S::copy_tile(lds + slot * S::kTileBytes, k + (it.sh * seq + (int64_t)j * BLK + piece * KC) * HD, tid);
+    S::copy_tile_buf(lds + slot * S::kTileBytes, rk, (uint32_t)((j * BLK + piece * KC) * S::kRowBytes), wave, lane);
   }
   __device__ void copy_v(const Item &it, int j, int piece, int slot) {
-    S::copy_tile(lds + slot * S::kTileBytes, v + (it.sh * seq + (int64_t)j * BLK + piece * KC) * HD, tid);
+    S::copy_tile_buf(lds + slot * S::kTileBytes, rv, (uint32_t)((j * BLK + piece * KC) * S::kRowBytes), wave, lane);
   }
   // dS^T[key][q] of every key of the piece (lane holds keys piece*KC + kb*16 + 4g + r of its
   // query of group rg): S^T from K and dP^T - D from V.
@@ -407,6 +418,8 @@ __global__ __launch_bounds__(BLK / (16 * dq_groups<T, BLK, HD>()) * 64, HD <= 64
   pol.scale = scale;
   pol.lds = lds;
   pol.tid = threadIdx.x;
+  pol.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  pol.lane = threadIdx.x & 63;
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
   pol.q_in_blk = (threadIdx.x >> 6) * 16 * R + pol.c;

@@ -148,19 +148,21 @@ struct AttnShape {
     }
   }
 
-  // Asynchronous copy of a KC x HD tile into LDS in the swizzled layout: every copy
-  // instruction fills 64 consecutive 16-byte LDS slots, so each lane fetches the global
-  // chunk whose swizzled home is its slot.  kTileCopies instructions per thread.
+  // Asynchronous copy of a KC x HD tile into LDS in the swizzled layout, through a buffer
+  // resource `r` over one tensor slice, the tile starting `soff` bytes into it: every copy
+  // instruction fills 64 consecutive 16-byte LDS slots, so each lane fetches the chunk
+  // whose swizzled home is its slot.  `wave` is wave-uniform (a scalar), so only the
+  // loop-invariant lane offsets live in vector registers.  kTileCopies instructions per
+  // thread.
   static constexpr int kTileCopies = kChunksPerThread;
-  __device__ static __forceinline__ void copy_tile(unsigned char *lds, const T *src, int tid) {
-    const int wave = tid >> 6, lane = tid & 63;
-    const unsigned char *g = reinterpret_cast<const unsigned char *>(src);
+  __device__ static __forceinline__ void copy_tile_buf(unsigned char *lds, rsrc_t r, uint32_t soff, int wave,
+                                                       int lane) {
 #pragma unroll
     for (int it = 0; it < kTileCopies; ++it) {
-      const int first = it * kThreads + wave * 64;          // first slot of this instruction
-      const int slot = first + lane;
+      const int first = it * kThreads + wave * 64;
+      const int slot = it * kThreads + (lane & 63) + wave * 64;
       const int row = slot / kChunks, phys = slot % kChunks;
-      copy16_to_lds(g + ((row * kChunks + (phys ^ swz(row))) << 4), lds + (first << 4));
+      buf_copy16_to_lds(r, (uint32_t)((row * kChunks + (phys ^ swz(row))) << 4), soff, lds + (first << 4));
     }
   }
 

@@ -73,12 +73,17 @@ struct FwdPolicy {
   float sl2;
   unsigned char *lds;
   int tid, c, g, q0;   // q0: this lane's query of group 0 in the block; group r: q0 + 16 r
+  int wave, lane;      // wave: wave-uniform
+  rsrc_t rk, rv;       // K and V of the item's (sample, head)
 
   typename S::QFrag qf[R];
   f32x4 acc[R][S::kDB];
   float m_run[R], l_part[R];
 
   __device__ void operands(const Item &it) {
+    const int64_t slice = seq * HD;
+    rk = make_rsrc(k + it.sh * slice, (uint32_t)(slice * sizeof(T)));
+    rv = make_rsrc(v + it.sh * slice, (uint32_t)(slice * sizeof(T)));
     const int64_t row0 = it.sh * seq + (int64_t)it.blk * BLK + q0;
 #pragma unroll
     for (int r = 0; r < R; ++r) S::load_row_frag(qf[r], q + (row0 + 16 * r) * HD, g);
@@ -94,10 +99,10 @@ struct FwdPolicy {
   }
   static constexpr bool kFreeK = true;   // K_j is done once the scores are
   __device__ void copy_k(const Item &it, int j, int piece, int slot) {
-    S::copy_tile(lds + slot * S::kTileBytes, k + (it.sh * seq + (int64_t)j * BLK + piece * KC) * HD, tid);
+    S::copy_tile_buf(lds + slot * S::kTileBytes, rk, (uint32_t)((j * BLK + piece * KC) * S::kRowBytes), wave, lane);
   }
   __device__ void copy_v(const Item &it, int j, int piece, int slot) {
-    S::copy_tile(lds + slot * S::kTileBytes, v + (it.sh * seq + (int64_t)j * BLK + piece * KC) * HD, tid);
+    S::copy_tile_buf(lds + slot * S::kTileBytes, rv, (uint32_t)((j * BLK + piece * KC) * S::kRowBytes), wave, lane);
   }
   // S^T tiles: lane holds keys piece*KC + kb*16 + 4g + rr of query q0 + 16 r.
   f32x4 st[R][S::kKB];
@@ -187,6 +192,8 @@ __global__ __launch_bounds__((BLK / (16 * fwd_groups<T, BLK, HD>()) * 64),
   pol.sl2 = sl2;
   pol.lds = lds;
   pol.tid = threadIdx.x;
+  pol.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  pol.lane = threadIdx.x & 63;
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
   pol.q0 = (threadIdx.x >> 6) * 16 * R + pol.c;

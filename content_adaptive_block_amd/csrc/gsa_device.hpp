@@ -62,19 +62,29 @@ __device__ __forceinline__ bf16_t to_bf16(float x) { return (bf16_t)x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
 
 // ---------------------------------------------------------------------------------------
-// Asynchronous global -> LDS copies.  global_load_lds_dword{,x4} writes each active lane's
-// 4 or 16 bytes to LDS at (wave-uniform base) + lane * size; completion is tracked by
-// the wave's vmcnt like any vector load.  The compiler does not track which LDS bytes a
-// copy writes, so every read of copied data is preceded by an explicit vmcnt wait (and a
-// barrier, for the other waves' copies).
+// Asynchronous global -> LDS copies through a buffer resource.  buffer_load_dword{,x4}
+// with the lds flag writes each active lane's 4 or 16 bytes to LDS at (wave-uniform
+// base) + lane * size; completion is tracked by the wave's vmcnt like any vector load.
+// The resource (four scalar registers) holds the base and size of one tensor slice, the
+// per-lane byte offset is a vector register that stays the same from copy to copy and
+// the slice offset of the tile is a scalar, so a copy needs no vector address
+// arithmetic; reads past the resource's size return zero.  The compiler does not track
+// which LDS bytes a copy writes, so every read of copied data is preceded by an explicit
+// vmcnt wait (and a barrier, for the other waves' copies).  Slice offsets are 32-bit:
+// the largest slice of the built instances (131072 tokens x 128 bf16 features) is 32 MiB.
 // ---------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
-
-__device__ __forceinline__ void copy16_to_lds(const void *g, unsigned char *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// gfx9 buffer descriptor word 3: 32-bit data format (dword accesses), no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
 }
-__device__ __forceinline__ void copy4_to_lds(const void *g, unsigned char *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+__device__ __forceinline__ void buf_copy16_to_lds(rsrc_t r, uint32_t voff, uint32_t soff, unsigned char *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf_copy4_to_lds(rsrc_t r, uint32_t voff, uint32_t soff, unsigned char *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 4, voff, soff, 0, 0);
 }
 
 // s_waitcnt immediate for "vmcnt <= n" leaving the other counters alone (gfx9 encoding:
