@@ -502,7 +502,8 @@ def measure(torch, gsa, wl, dev, c, t, flush, steps: int, warmup: int, settle_ms
            "kept_tiles": tiles, "literal_blocks": path.mask.n_literal.cpu().numpy()[:wl.batch].tolist(),
            "kernels": kernel_table(wl, kern, tiles), "roofline": roofline(wl, kern, tiles)}
     if warm_steps > 0:
-        w_ms, w_kern = path.time(warm_steps, warmup, 0.0)
+        # back-to-back steps draw more power than cold ones: settle again before timing them
+        w_ms, w_kern = path.time(warm_steps, warmup, settle_ms)
         rec["warm"] = {"ms_per_step": round(w_ms, 4), "tflops": round(fl * tiles / (w_ms * 1e-3) / 1e12, 3),
                        "kernels_ms": {nm: round(v, 4) for nm, v in w_kern.items()}}
     return path, rec
