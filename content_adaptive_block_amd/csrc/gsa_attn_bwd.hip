@@ -94,6 +94,12 @@ constexpr int dkdv_groups() {
 #ifndef GSA_DKDV_PIECE
 #define GSA_DKDV_PIECE 32
 #endif
+// LDS stages of dK/dV at b = 64 (32-row query pieces): three let every copy run two
+// pieces ahead of its use at the same six workgroups per CU (24.75 KiB each); dK/dV
+// 167.2-170.3 vs 169.1-171.7 us at 8 x 8 KiB over three interleaved runs.
+#ifndef GSA_DKDV_STAGES
+#define GSA_DKDV_STAGES 3
+#endif
 template <typename T, int BLK, int HD>
 constexpr int dkdv_piece_rows() {
   if (std::is_same<T, bf16_t>::value && BLK == 64 && HD == 64) return GSA_DKDV_PIECE;
@@ -113,6 +119,12 @@ struct DkdvPolicy {
   static constexpr int kStageBytes = 2 * S::kTileBytes + 2 * KQ * 4;
   static constexpr int kVecLanes = KQ / S::kWaves;   // floats of LSE_i (and D_i) per wave
   static_assert(kVecLanes <= 64, "vector slice per wave");
+  // LDS stages: three (copies two pieces ahead) where pieces are small, else two.
+  static constexpr int kStages = kSub == 2 ? GSA_DKDV_STAGES : 2;
+  // Vector memory instructions per piece and wave: the Q and dO tiles, LSE and D (every
+  // wave has lanes below kVecLanes, so every wave issues both vector copies).
+  static constexpr int kCopyOps = 2 * S::kTileCopies + 2;
+  static_assert(kVecLanes >= 1, "every wave copies part of LSE and D");
 
   const T *q, *k, *v, *dout;
   const float *lse, *dvec;
@@ -159,7 +171,9 @@ struct DkdvPolicy {
       }
   }
   __device__ void copy(const Item &it, int i, int piece, int stage) {
-    unsigned char *dst = lds + stage * kStageBytes;
+    copy_to(lds + stage * kStageBytes, it, i, piece);
+  }
+  __device__ __forceinline__ void copy_to(unsigned char *dst, const Item &, int i, int piece) {
     const int r0 = i * BLK + piece * KQ;   // first row of the piece in the (sample, head) slice
     S::copy_tile_buf(dst, rq, (uint32_t)(r0 * S::kRowBytes), wave, lane);
     S::copy_tile_buf(dst + S::kTileBytes, rdo, (uint32_t)(r0 * S::kRowBytes), wave, lane);
@@ -170,7 +184,18 @@ struct DkdvPolicy {
     }
   }
   __device__ void compute(const Item &it, int e, int piece, int stage) {
-    const unsigned char *lq = lds + stage * kStageBytes;
+    compute_at(lds + stage * kStageBytes, it, e, piece);
+  }
+  // One step of the three-stage pipeline: copy piece `piece` of query block j_next into the
+  // stage at `wr` (when do_copy) and compute piece `piece` of entry e from the stage at
+  // `rd`.  The two stages never overlap; saying so (restrict) lets the compiler keep the
+  // step's LDS reads from waiting for the copies just issued.
+  __device__ __forceinline__ void step(unsigned char *__restrict__ wr, const unsigned char *__restrict__ rd,
+                                       const Item &it, int e, int piece, bool do_copy, int j_next) {
+    if (do_copy) copy_to(wr, it, j_next, piece);
+    compute_at(rd, it, e, piece);
+  }
+  __device__ __forceinline__ void compute_at(const unsigned char *lq, const Item &it, int e, int piece) {
     const unsigned char *ldo = lq + S::kTileBytes;
     const float *ll = reinterpret_cast<const float *>(lq + 2 * S::kTileBytes);
     const float *ld = ll + KQ;
@@ -235,7 +260,7 @@ __global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64),
     WorkLists wl, float sl2, float scale) {
   constexpr int R = dkdv_groups<T, BLK, HD>();
   using P = DkdvPolicy<T, BLK, HD, R>;
-  __shared__ __align__(16) unsigned char lds[2 * P::kStageBytes];
+  __shared__ __align__(16) unsigned char lds[P::kStages * P::kStageBytes];
   const WorkItem it = wl.decode(dispatch_position(blockIdx.x, gridDim.x));
 
   P pol;
@@ -257,7 +282,11 @@ __global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64),
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
   pol.key0 = (threadIdx.x >> 6) * 16 * R + pol.c;
-  run_item(pol, it);
+  if constexpr (P::kStages == 3) {
+    run_item3(pol, it);
+  } else {
+    run_item(pol, it);
+  }
 }
 
 // 16-row query groups per wave in dQ.  At b = d = 128 eight one-group waves read 768 KiB

@@ -349,6 +349,50 @@ __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
 
 
 // ---------------------------------------------------------------------------------------
+// run_item with three LDS stages for items whose entries arrive as two pieces: the copies
+// of a piece are issued two pieces ahead (one entry), so each has two steps to land.  A
+// step waits only for its own piece (the wave's kCopyOps newer copy instructions may stay
+// in flight), synchronises -- after which every wave has finished the previous step, so
+// that step's stage is free -- and calls pol.step(write stage, read stage, ...), which
+// issues the copies of the same piece of the next entry into the free stage and computes.
+// ---------------------------------------------------------------------------------------
+template <class P>
+__device__ __forceinline__ void run_item3(P &pol, const WorkItem &it) {
+  static_assert(P::kSub == 2 && P::kStages == 3, "two pieces per entry, three stages");
+  const int lane = threadIdx.x & (kWave - 1);
+  int chunk = it.beg + 1 + lane < it.end ? it.list[it.beg + 1 + lane] : 0;
+  pol.operands(it);
+  pol.copy(it, it.first, 0, 0);
+  pol.copy(it, it.first, 1, 1);
+  pol.begin(it);
+  int stage = 0;
+  for (int e = it.beg; e < it.end; ++e) {
+    const bool more = e + 1 < it.end;
+    int j_next = 0;
+    if (more) {
+      const int nx = e - it.beg;   // position of entry e + 1 after the first
+      if (nx > 0 && (nx & (kWave - 1)) == 0)
+        chunk = e + 1 + lane < it.end ? it.list[e + 1 + lane] : 0;
+      j_next = __builtin_amdgcn_readlane(chunk, nx & (kWave - 1));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // In flight before this wait: piece (e, h), then (e, 1) or, at h = 1, (e + 1, 0).
+      if (h == 0 || more) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(P::kCopyOps));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      wg_barrier();
+      const int ws = stage == 0 ? 2 : stage - 1;   // the stage of the previous step
+      pol.step(pol.lds + ws * P::kStageBytes, pol.lds + stage * P::kStageBytes, it, e, h, more, j_next);
+      stage = stage == 2 ? 0 : stage + 1;
+    }
+  }
+  pol.finish(it);
+}
+
+// ---------------------------------------------------------------------------------------
 // Three-slot pipeline for items whose two streamed tiles (K_j and V_j) are used one after
 // the other: 3 tiles of LDS instead of 4, which lets 6 rather than 4 workgroups share a
 // CU (gfx950 fits six 24 KiB workgroups but only four 32 KiB ones).  Each list entry is
