@@ -51,15 +51,15 @@ __device__ __forceinline__ int order_key(int len) { return len <= 0 ? 0 : 32 - _
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
-// First index x in [0, n) with start[x + 1] > e, for strictly increasing start[0..n].
+// Largest x in [0, n) with start[x] <= e, for strictly increasing start[0..n] with
+// start[0] = 0 <= e: a fixed number of halving steps (n <= GSA_MAX_BLOCKS), so the
+// searches of several lists have no data-dependent loop and can be interleaved.
 __device__ __forceinline__ int find_segment(const int *start, int n, int e) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (start[mid] <= e) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
+  int x = 0;
+#pragma unroll
+  for (int step = GSA_MAX_BLOCKS / 2; step > 0; step >>= 1)
+    if (x + step < n && start[x + step] <= e) x += step;
+  return x;
 }
 
 // From the six list lengths of this thread's block t (rows of classes 0..2, then columns):
@@ -69,7 +69,8 @@ __device__ __forceinline__ int find_segment(const int *start, int n, int e) {
 __device__ void lengths_to_lists(const int (&len)[6], int n, int64_t s, int64_t batch, int32_t *__restrict__ row_ptr,
                                  int32_t *__restrict__ col_ptr, int64_t *__restrict__ n_edges,
                                  int32_t *__restrict__ sched, int (*s_start)[GSA_MAX_BLOCKS + 1],
-                                 int (*s_wave)[kMaskWaves], int (*s_cnt)[kMaskWaves][kOrderKeys]) {
+                                 int (*s_wave)[kMaskWaves], int (*s_cnt)[kMaskWaves][kOrderKeys],
+                                 bool writer = true) {
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const bool valid = t < n;
   const int active = (n + kWave - 1) / kWave;
@@ -121,7 +122,7 @@ __device__ void lengths_to_lists(const int (&len)[6], int n, int64_t s, int64_t 
       s_cnt[q][w2][kk] = run;
       run += v;
     }
-    hist[(((q / 3) * batch + s) * 3 + q % 3) * kOrderKeys + kk] = run;
+    if (writer) hist[(((q / 3) * batch + s) * 3 + q % 3) * kOrderKeys + kk] = run;
   }
 #pragma unroll
   for (int q = 0; q < 6 && busy; ++q) {
@@ -134,17 +135,17 @@ __device__ void lengths_to_lists(const int (&len)[6], int n, int64_t s, int64_t 
     const int start = base + incl[q] - len[q];
     int32_t *ptr = (q < 3 ? row_ptr : col_ptr) + (s * 3 + q % 3) * (int64_t)(n + 1);
     if (valid) {
-      ptr[t] = start;
+      if (writer) ptr[t] = start;
       s_start[q][t] = start;
     }
     if (t == 0) {
-      ptr[n] = tot;
+      if (writer) ptr[n] = tot;
       s_start[q][n] = tot;
-      if (q < 3) n_edges[s * 3 + q] = tot;
+      if (writer && q < 3) n_edges[s * 3 + q] = tot;
     }
   }
   __syncthreads();
-  if (valid) {
+  if (valid && writer) {
 #pragma unroll
     for (int q = 0; q < 6; ++q)
       packed[(((q / 3) * batch + s) * 3 + q % 3) * (int64_t)n + t] =
@@ -167,6 +168,9 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
 
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int64_t s = blockIdx.x;
+  // gridDim.y workgroups share a sample: each derives its flags and list starts, the first
+  // writes them, and all write a share of the list entries.
+  const bool writer = blockIdx.y == 0;
   const bool valid = t < n;
   // Waves holding blocks; the others only help with the list entries.
   const int active = (n + kWave - 1) / kWave;
@@ -198,13 +202,13 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
   }
   const int rank = wave_base + below;   // literal blocks j < t
   if (valid) {
-    flags[s * n + t] = lit ? 1 : 0;
+    if (writer) flags[s * n + t] = lit ? 1 : 0;
     s_prefix[t] = rank;
     if (lit) s_list[rank] = t;
   }
   if (t == 0) {
     s_prefix[n] = n_lit;
-    n_literal[s] = n_lit;
+    if (writer) n_literal[s] = n_lit;
   }
   __syncthreads();
 
@@ -224,51 +228,61 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(
     len[5] = cwin + (lit ? n_lit - s_prefix[beyond] : 0);
   }
 
-  lengths_to_lists(len, n, s, batch, row_ptr, col_ptr, n_edges, sched, s_start, s_wave, s_cnt);
+  lengths_to_lists(len, n, s, batch, row_ptr, col_ptr, n_edges, sched, s_start, s_wave, s_cnt, writer);
 
-  // List entries, one thread each.  Row i of class k, entry e of it:
+  // List entries, one thread each; the six lists are walked together so that their row
+  // searches interleave.  Entry e of row i (lists 0-2, col_idx) or of column j (lists
+  // 3-5, row_idx) of class k:
+  //   row i:    local lo + e; literal: s_list[e] if l_i, else i; hybrid: the literal
+  //             j < lo first, then lo + ...   (lo = max(0, i - w))
+  //   column j: local j + e; literal: s_list[prefix_j + e] if l_j, else j; hybrid:
+  //             j .. j + w first, then the literal i > j + w
+  int tot[6], most = 0;
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    int32_t *out = col_idx + (s * 3 + k) * cap;
-    const int total = s_start[k][n];
-    for (int e0 = t; e0 < total; e0 += kMaskThreads) {
-      const int i = find_segment(s_start[k], n, e0);
-      const int e = e0 - s_start[k][i];
-      const int lo = i - ww > 0 ? i - ww : 0;
-      const bool li = s_prefix[i + 1] != s_prefix[i];
-      int j;
-      if (k == 0) {
-        j = lo + e;
-      } else if (k == 1) {
-        j = li ? s_list[e] : i;
-      } else {
-        const int n_far = li ? s_prefix[lo] : 0;   // literal j < i - w
-        j = e < n_far ? s_list[e] : lo + (e - n_far);
-      }
-      out[e0] = j;
-    }
+  for (int q = 0; q < 6; ++q) {
+    tot[q] = s_start[q][n];
+    most = tot[q] > most ? tot[q] : most;
   }
-  // Column j of class k, entry e of it:
+  const int stride = kMaskThreads * (int)gridDim.y;
+  for (int e0 = (int)blockIdx.y * kMaskThreads + t; e0 < most; e0 += stride) {
+    int seg[6];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    int32_t *out = row_idx + (s * 3 + k) * cap;
-    const int total = s_start[3 + k][n];
-    for (int e0 = t; e0 < total; e0 += kMaskThreads) {
-      const int j = find_segment(s_start[3 + k], n, e0);
-      const int e = e0 - s_start[3 + k][j];
-      const bool lj = s_prefix[j + 1] != s_prefix[j];
-      int i;
-      if (k == 0) {
-        i = j + e;
-      } else if (k == 1) {
-        i = lj ? s_list[s_prefix[j] + e] : j;
-      } else {
-        const int after = n - 1 - j;
-        const int cwin = (after < ww ? after : ww) + 1;
-        const int first_far = s_prefix[j + ww + 1 < n ? j + ww + 1 : n];
-        i = e < cwin ? j + e : s_list[first_far + (e - cwin)];
+    for (int q = 0; q < 6; ++q) seg[q] = e0 < tot[q] ? find_segment(s_start[q], n, e0) : 0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      if (e0 < tot[k]) {
+        const int i = seg[k];
+        const int e = e0 - s_start[k][i];
+        const int lo = i - ww > 0 ? i - ww : 0;
+        const bool li = s_prefix[i + 1] != s_prefix[i];
+        int j;
+        if (k == 0) {
+          j = lo + e;
+        } else if (k == 1) {
+          j = li ? s_list[e] : i;
+        } else {
+          const int n_far = li ? s_prefix[lo] : 0;   // literal j < i - w
+          j = e < n_far ? s_list[e] : lo + (e - n_far);
+        }
+        col_idx[(s * 3 + k) * cap + e0] = j;
       }
-      out[e0] = i;
+      if (e0 < tot[3 + k]) {
+        const int j = seg[3 + k];
+        const int e = e0 - s_start[3 + k][j];
+        const bool lj = s_prefix[j + 1] != s_prefix[j];
+        int i;
+        if (k == 0) {
+          i = j + e;
+        } else if (k == 1) {
+          i = lj ? s_list[s_prefix[j] + e] : j;
+        } else {
+          const int after = n - 1 - j;
+          const int cwin = (after < ww ? after : ww) + 1;
+          const int first_far = s_prefix[j + ww + 1 < n ? j + ww + 1 : n];
+          i = e < cwin ? j + e : s_list[first_far + (e - cwin)];
+        }
+        row_idx[(s * 3 + k) * cap + e0] = i;
+      }
     }
   }
 }
@@ -585,9 +599,17 @@ static gsa_status launch_order(const gsa_mask &m, hipStream_t stream) {
   return check_launch("order_scatter_kernel");
 }
 
+// Workgroups per sample in mask_kernel: enough that each writes at most about 4K entries
+// of the up to 6 N (N + 1) / 2 list entries of a sample (1 at N <= 64, 32 at N = 512).
+static int mask_split(int n) {
+  const int64_t cap = mask_cap(n);
+  const int64_t split = cap / 4096;
+  return (int)(split < 1 ? 1 : (split > 32 ? 32 : split));
+}
+
 gsa_status launch_build_mask(const int32_t *c, const gsa_mask &m, hipStream_t stream) {
   const int n = m.n_blocks;
-  hipLaunchKernelGGL(mask_kernel, dim3((unsigned)m.batch), dim3(kMaskThreads), 0, stream, c, n,
+  hipLaunchKernelGGL(mask_kernel, dim3((unsigned)m.batch, (unsigned)mask_split(n)), dim3(kMaskThreads), 0, stream, c, n,
                      m.window, m.flags, m.n_literal, m.row_ptr, m.col_idx, m.col_ptr, m.row_idx,
                      m.n_edges, mask_cap(n), m.sched, m.batch);
   gsa_status st = check_launch("mask_kernel");
