@@ -509,6 +509,44 @@ def measure(torch, gsa, wl, dev, c, t, flush, steps: int, warmup: int, settle_ms
     return path, rec
 
 
+def sdpa_dense(torch, t, flush, steps: int):
+    """Dense causal attention through torch's scaled_dot_product_attention with only its
+    flash or memory-efficient backend allowed (whichever runs and is faster), forward and
+    backward on the workload's Q, K, V, dO, each step after the cache flush.  None when
+    neither backend is available."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    best = None
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            q, k, v = (t[nm].detach().clone().requires_grad_(True) for nm in ("q", "k", "v"))
+            with sdpa_kernel([be]):
+                for _ in range(2):
+                    F.scaled_dot_product_attention(q, k, v, is_causal=True).backward(t["do"])
+                torch.cuda.synchronize()
+                fw, bw = [], []
+                for _ in range(steps):
+                    q.grad = k.grad = v.grad = None
+                    flush()
+                    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                    e[0].record()
+                    o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+                    e[1].record()
+                    o.backward(t["do"])
+                    e[2].record()
+                    torch.cuda.synchronize()
+                    fw.append(e[0].elapsed_time(e[1]))
+                    bw.append(e[1].elapsed_time(e[2]))
+            rec = {"backend": name, "fwd_ms": round(float(np.median(fw)), 4), "bwd_ms": round(float(np.median(bw)), 4)}
+            rec["ms_per_step"] = round(rec["fwd_ms"] + rec["bwd_ms"], 4)
+            if best is None or rec["ms_per_step"] < best["ms_per_step"]:
+                best = rec
+            del q, k, v
+        except RuntimeError:
+            continue
+    return best
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -525,6 +563,9 @@ def main():
                     help="also time this many steps of the dense causal variant for comparison (0: skip)")
     ap.add_argument("--bigbird-steps", type=int, default=10,
                     help="steps of a BigBird-style fixed mask at the same shape, for comparison (0: skip)")
+    ap.add_argument("--sdpa-steps", type=int, default=5,
+                    help="cold fwd+bwd steps of torch SDPA (flash / memory-efficient backends) as dense causal "
+                         "attention at the same shape, for comparison (0: skip)")
     ap.add_argument("--layer-steps", type=int, default=5,
                     help="fwd+bwd steps of the ByteLM attention layer (projections + kernels) (0: skip)")
     ap.add_argument("--pipeline-steps", type=int, default=20,
@@ -715,6 +756,16 @@ def main():
                  "sparse_speedup": round(d_ms / ms_step, 2)}
         del dpath
 
+    # The vendor library's dense causal attention at the same shape (torch SDPA restricted
+    # to its flash and memory-efficient backends, never the math path), forward and
+    # backward, cold steps like ours: context for the dense figure above.
+    sdpa = None
+    if args.sdpa_steps > 0 and wl.dtype == "bf16" and wl.backward:
+        sdpa = sdpa_dense(torch, t, flush, args.sdpa_steps)
+        if sdpa is not None:
+            sdpa["this_library_dense_ms"] = dense["ms_per_step"] if dense else None
+            sdpa["gzip_sparse_speedup"] = round(sdpa["ms_per_step"] / ms_step, 2)
+
     n_edges = mask.n_edges.cpu().numpy().reshape(wl.batch, 3)
     rec = {
         "metric": METRIC, "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -731,7 +782,7 @@ def main():
         "kept_tiles": head["kept_tiles"], "literal_blocks": head["literal_blocks"],
         "host_prepare_ms": {"all_cores": round(prep_ms, 3), "one_thread": round(prep1_ms, 3)},
         "kernels": head["kernels"], "roofline": head["roofline"], "warm": head.get("warm"), "dense_causal": dense,
-        "host_pipeline": pipeline, "layer": layer, "bigbird": bigbird,
+        "host_pipeline": pipeline, "layer": layer, "bigbird": bigbird, "torch_sdpa_dense": sdpa,
         "n_edges": n_edges.tolist(),
         "env": {"gpu": torch.cuda.get_device_name(dev), "hip": torch.version.hip, "torch": torch.__version__,
                 "zlib": gsa.zlib_version(), "host_cpus": os.cpu_count(),
