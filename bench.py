@@ -12,9 +12,12 @@ The headline workload is 8 samples x 8192 bytes, block 64, window 2, 12 heads (6
 text-like bytes (the pages' PG-19 runs at 8K bytes are the shape it stands in for).
 
 Timing: the primary figures are cold-cache steps.  Before each step a 512 MiB buffer
-(larger than the 256 MB Infinity Cache) is written, outside the events that time the
-step; HIP events on the launch stream mark the step's start and the end of every
-kernel.  The device first runs ``--settle-ms`` of such steps untimed (its clocks settle
+(larger than the 256 MB Infinity Cache) is read, outside the events that time the step,
+so that no line of the workload's tensors is cached when it starts; HIP events on the
+launch stream mark the step's start and the end of every kernel.  The flush reads
+rather than writes: a written buffer leaves the Infinity Cache full of dirty lines, and
+the step's first kernel then pays for writing them back to HBM (``cold_write_fill``
+reports the step time under that protocol).  The device first runs ``--settle-ms`` of such steps untimed (its clocks settle
 under sustained load), then ``--warmup`` steps, then ``--steps`` timed steps; the step
 time is their median.  ``warm`` gives the same for back-to-back steps with nothing in
 between (secondary).
@@ -393,8 +396,8 @@ class DevicePath:
         return spent
 
     def time_cold(self, steps: int, warmup: int, settle_ms: float, flush):
-        """Cold-cache steps: ``flush`` (a callable that writes more than the Infinity Cache
-        holds) runs before every step, outside the events around it.  ``settle_ms`` of device
+        """Cold-cache steps: ``flush`` (a callable that reads, or writes, more than the
+        Infinity Cache holds) runs before every step, outside the events around it.  ``settle_ms`` of device
         time in such steps and ``warmup`` more run untimed first.  Returns (median ms per
         step, mean ms per step, mean ms per kernel, per-step ms list)."""
         torch = self.torch
@@ -483,10 +486,13 @@ def workload_name(wl) -> str:
             f"{wl.dtype}, {'fwd+bwd' if wl.backward else 'fwd'}")
 
 
-def measure(torch, gsa, wl, dev, c, t, flush, steps: int, warmup: int, settle_ms: float, warm_steps: int = 0):
+def measure(torch, gsa, wl, dev, c, t, flush, steps: int, warmup: int, settle_ms: float, warm_steps: int = 0,
+            fill=None, fill_steps: int = 0):
     """Cold steps (primary) and ``warm_steps`` back-to-back steps of one workload:
     (DevicePath, record).  The record holds the step times, per-kernel times, effective
-    TFLOP/s and the dominant kernel's roofline, all from the cold steps."""
+    TFLOP/s and the dominant kernel's roofline, all from the cold steps.  With ``fill``
+    (a callable that writes more than the Infinity Cache holds), ``fill_steps`` more cold
+    steps run after it instead of ``flush`` (``cold_write_fill``)."""
     path = DevicePath(torch, gsa, wl, c, t, dev)
     med, mean, kern, step_ms = path.time_cold(steps, warmup, settle_ms, flush)
     n_edges = path.mask.n_edges.cpu().numpy().reshape(wl.batch, 3)
@@ -506,6 +512,11 @@ def measure(torch, gsa, wl, dev, c, t, flush, steps: int, warmup: int, settle_ms
         w_ms, w_kern = path.time(warm_steps, warmup, settle_ms)
         rec["warm"] = {"ms_per_step": round(w_ms, 4), "tflops": round(fl * tiles / (w_ms * 1e-3) / 1e12, 3),
                        "kernels_ms": {nm: round(v, 4) for nm, v in w_kern.items()}}
+    if fill is not None and fill_steps > 0:
+        f_med, _, f_kern, _ = path.time_cold(fill_steps, warmup, settle_ms / 2, fill)
+        rec["cold_write_fill"] = {"ms_per_step": round(f_med, 4),
+                                  "tflops": round(fl * tiles / (f_med * 1e-3) / 1e12, 3),
+                                  "kernels_ms": {nm: round(v, 4) for nm, v in f_kern.items()}}
     return path, rec
 
 
@@ -575,6 +586,8 @@ def main():
     ap.add_argument("--other-steps", type=int, default=20)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain elementwise copy of this many MiB 3 times (HBM counter calibration)")
+    ap.add_argument("--fill-steps", type=int, default=20,
+                    help="cold steps after a 512 MiB write instead of the read flush (cold_write_fill; 0: none)")
     ap.add_argument("--warm-steps", type=int, default=-1,
                     help="back-to-back (warm) steps timed after the cold ones (-1: as many as --steps; 0: none)")
     ap.add_argument("--trace-from", metavar="KERNEL_TRACE_CSV",
@@ -632,13 +645,20 @@ def main():
         gsa.gsa_prepare(x, wl.block, n_threads=1)
     prep1_ms = (time.perf_counter() - t0) / 3 * 1e3
 
-    flush_buf = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    # Cache flush: a 512 MiB buffer, written once here, then read before every cold step
+    # (a sum into a preallocated scalar): the caches end up holding its clean lines only.
+    flush_buf = torch.ones(512 << 18, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def flush():
+        torch.sum(flush_buf, dim=0, dtype=torch.float32, out=flush_sink)
+
+    def fill():   # the write-fill protocol, for cold_write_fill
         flush_buf.fill_(1.0)
 
     warm_steps = args.steps if args.warm_steps < 0 else args.warm_steps
-    path, head = measure(torch, gsa, wl, dev, c, t, flush, args.steps, args.warmup, args.settle_ms, warm_steps)
+    path, head = measure(torch, gsa, wl, dev, c, t, flush, args.steps, args.warmup, args.settle_ms, warm_steps,
+                         fill=fill, fill_steps=args.fill_steps)
     ms_step = head["ms_per_step"]
     kern_ms = {nm: v["ms"] for nm, v in head["kernels"].items()}
     mask = path.mask
@@ -773,7 +793,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": head["workload"], "global_batch": wl.batch, "seq_len": wl.seq_len,
                    "parallelism": "single GPU"},
-        "timing": "cold: 512 MiB written before every step, outside its events; median of the timed steps",
+        "timing": "cold: 512 MiB read before every step, outside its events; median of the timed steps",
+        "cold_write_fill": head.get("cold_write_fill"),
         "ms_per_step_mean": head["ms_per_step_mean"], "ms_per_step_min": head["ms_per_step_min"],
         "fwd_ms": round(kern_ms["fwd"], 4), "bwd_ms": round(sum(kern_ms.get(nm, 0.0) for nm in ("bwd_dq", "bwd_dkdv")), 4),
         "mask_ms": round(kern_ms["mask"], 4),

@@ -25,7 +25,7 @@
 //   * Only the diagonal block applies the token-causal mask.  Rows are never empty: the
 //     diagonal block is always kept and a query always sees itself.
 //   * Workgroups run in the mask kernel's work order (longest rows first, by octave of
-//     length), runs of 16 consecutive items per XCD.
+//     length), runs of 8 consecutive items per XCD.
 #include <type_traits>
 
 #include "gsa_attn_common.hpp"
