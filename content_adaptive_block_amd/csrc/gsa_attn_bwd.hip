@@ -183,9 +183,6 @@ struct DkdvPolicy {
       buf_copy4_to_lds(rd, x4, (uint32_t)(r0 * 4), dst + 2 * S::kTileBytes + KQ * 4 + wave * kVecLanes * 4);
     }
   }
-  __device__ void compute(const Item &it, int e, int piece, int stage) {
-    compute_at(lds + stage * kStageBytes, it, e, piece);
-  }
   // One step of the three-stage pipeline: copy piece `piece` of query block j_next into the
   // stage at `wr` (when do_copy) and compute piece `piece` of entry e from the stage at
   // `rd`.  The two stages never overlap; saying so (restrict) lets the compiler keep the
@@ -193,6 +190,14 @@ struct DkdvPolicy {
   __device__ __forceinline__ void step(unsigned char *__restrict__ wr, const unsigned char *__restrict__ rd,
                                        const Item &it, int e, int piece, bool do_copy, int j_next) {
     if (do_copy) copy_to(wr, it, j_next, piece);
+    compute_at(rd, it, e, piece);
+  }
+  // The same for the two-stage pipeline, whose copy is of another piece (`copy_piece` of
+  // block `j_copy`).
+  __device__ __forceinline__ void step_to(unsigned char *__restrict__ wr, const unsigned char *__restrict__ rd,
+                                          const Item &it, int e, int piece, bool do_copy, int j_copy,
+                                          int copy_piece) {
+    if (do_copy) copy_to(wr, it, j_copy, copy_piece);
     compute_at(rd, it, e, piece);
   }
   __device__ __forceinline__ void compute_at(const unsigned char *lq, const Item &it, int e, int piece) {
@@ -406,8 +411,15 @@ struct DqPolicy {
     }
   }
   // dQ^T += K^T dS^T over the piece, one part of 16*kPartTiles keys at a time.
-  __device__ void compute_b(const Item &, int, int, int k_slot, int) {
-    const unsigned char *lk = lds + k_slot * S::kTileBytes;
+  // The second half of a step: the next piece's V into `wr` (when `more`), then dQ from
+  // this piece's K at `rd`; the slots never overlap (restrict: the transposing reads of K
+  // need not wait for the copy just issued).
+  __device__ __forceinline__ void step_b(unsigned char *__restrict__ wr, const unsigned char *__restrict__ rd,
+                                         const Item &it, int e, int piece, bool more, int j_next, int h_next) {
+    if (more) S::copy_tile_buf(wr, rv, (uint32_t)((j_next * BLK + h_next * KC) * S::kRowBytes), wave, lane);
+    compute_b_at(rd, it, e, piece);
+  }
+  __device__ __forceinline__ void compute_b_at(const unsigned char *lk, const Item &, int, int) {
 #pragma unroll
     for (int part = 0; part < S::kParts; ++part)
       S::template accumulate_part_n<R>(&acc[0][0], lk, &dsr[0][part * S::kPartTiles], S::kKB, part, c, g);

@@ -307,15 +307,19 @@ struct AttnShape {
 // Per-item pipeline shared by the attention kernels.  A workgroup runs one work item,
 // which walks one list (a CSR row or a CSC column); each list entry's block arrives as
 // P::kSub pieces of BLK / kSub rows, each piece in one of two LDS stages by asynchronous
-// copies issued one piece ahead.  The policy P supplies kSub and:
+// copies issued one piece ahead.  The policy P supplies kSub, kStageBytes and:
 //   operands(item)                   load the item's register operands (before the loop)
 //   begin(item)                      clear the accumulators
 //   copy(item, block, piece, stage)  issue the copies of one piece into `stage`
-//   compute(item, e, piece, stage)   one piece of list entry e (e indexes item.list)
+//   step_to(write, read, item, e, piece, do_copy, block, copy_piece)
+//                                    copy piece `copy_piece` of `block` to the stage at
+//                                    `write` (when do_copy), then compute piece `piece` of
+//                                    list entry e from the stage at `read`
 //   finish(item)                     write the item's outputs
 // A step waits for its own copies, synchronises -- after which every wave has finished
 // the previous step, so the other stage is free -- issues the next piece's copies and
-// computes.
+// computes.  The two stage pointers are restrict, so that the compiler does not make the
+// step's LDS reads wait for the copies just issued.
 // ---------------------------------------------------------------------------------------
 template <class P>
 __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
@@ -334,15 +338,19 @@ __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
     for (int h = 0; h < kSub; ++h) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       wg_barrier();
+      bool do_copy = true;
+      int h_copy = h + 1;
       if (h + 1 < kSub) {
-        pol.copy(it, j, h + 1, stage ^ 1);
       } else if (e + 1 < it.end) {
         if (nx > 0 && (nx & (kWave - 1)) == 0)
           chunk = e + 1 + lane < it.end ? it.list[e + 1 + lane] : 0;
         j = __builtin_amdgcn_readlane(chunk, nx & (kWave - 1));
-        pol.copy(it, j, 0, stage ^ 1);
+        h_copy = 0;
+      } else {
+        do_copy = false;
       }
-      pol.compute(it, e, h, stage);
+      pol.step_to(pol.lds + (stage ^ 1) * P::kStageBytes, pol.lds + stage * P::kStageBytes, it, e, h, do_copy, j,
+                  h_copy);
       stage ^= 1;
     }
   }
@@ -403,10 +411,14 @@ __device__ __forceinline__ void run_item3(P &pol, const WorkItem &it) {
 //   wait for K and V, barrier (everyone left the previous piece, so the spare slot is
 //   free); copy the next piece's K into the spare slot; compute_a (reads K, and V if it
 //   wants); barrier (everyone is done with the slot the policy frees: K when kFreeK, else
-//   V); copy the next piece's V into it; compute_b.
+//   V); step_b: copy the next piece's V into it and compute the second half.
 // The policy supplies operands/begin/finish as for run_item, plus the constants kSub and
 // kFreeK, copy_k(item, j, piece, slot), copy_v(item, j, piece, slot),
-// compute_a(item, e, piece, k_slot, v_slot) and compute_b(item, e, piece, k_slot, v_slot).
+// compute_a(item, e, piece, k_slot, v_slot) and step_b(write, read, item, e, piece, more,
+// j_next, piece_next), which copies the next piece's V (when `more`) to `write` and computes
+// from the tile at `read` (V when kFreeK, else K).  The two pointers are restrict: the
+// second half's transposing LDS reads then need not wait for the copy just issued (3-5%
+// faster dQ at b = d = 128).
 // ---------------------------------------------------------------------------------------
 template <class P>
 __device__ __forceinline__ void run_item_ring(P &pol, const WorkItem &it) {
@@ -438,8 +450,8 @@ __device__ __forceinline__ void run_item_ring(P &pol, const WorkItem &it) {
       pol.compute_a(it, e, h, ks, vs);
       wg_barrier();
       const int freed = P::kFreeK ? ks : vs;
-      if (more) pol.copy_v(it, j_next, h_next, freed);
-      pol.compute_b(it, e, h, ks, vs);
+      pol.step_b(pol.lds + freed * P::S::kTileBytes, pol.lds + (P::kFreeK ? vs : ks) * P::S::kTileBytes, it, e, h,
+                 more, j_next, h_next);
       // The next piece's K sits in the spare slot and its V in the freed one; the other
       // is spare.
       const int next_spare = P::kFreeK ? vs : ks;

@@ -149,8 +149,15 @@ struct FwdPolicy {
         }
     }
   }
-  __device__ void compute_b(const Item &, int, int, int, int v_slot) {
-    const unsigned char *lv = lds + v_slot * S::kTileBytes;
+  // The second half of a step: the next piece's V into `wr` (when `more`), then P V from
+  // this piece's V at `rd`.  The slots never overlap; saying so (restrict) keeps the
+  // transposing reads from waiting for the copy just issued.
+  __device__ __forceinline__ void step_b(unsigned char *__restrict__ wr, const unsigned char *__restrict__ rd,
+                                         const Item &it, int e, int piece, bool more, int j_next, int h_next) {
+    if (more) S::copy_tile_buf(wr, rv, (uint32_t)((j_next * BLK + h_next * KC) * S::kRowBytes), wave, lane);
+    compute_b_at(rd, it, e, piece);
+  }
+  __device__ __forceinline__ void compute_b_at(const unsigned char *lv, const Item &, int, int) {
 #pragma unroll
     for (int part = 0; part < S::kParts; ++part)
       S::template accumulate_part_n<R>(&acc[0][0], lv, &st[0][part * S::kPartTiles], S::kKB, part, c, g);
