@@ -301,6 +301,13 @@ __global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64),
 #ifndef GSA_DQ_GROUPS_WIDE
 #define GSA_DQ_GROUPS_WIDE 2
 #endif
+// Four LDS slots at b = 128 (as for the forward): 2.94-2.96 vs 3.02-3.04 ms at 2 x 64 KiB.
+#ifndef GSA_DQ_RING4_WIDE
+#define GSA_DQ_RING4_WIDE 1
+#endif
+#ifndef GSA_DQ_RING4
+#define GSA_DQ_RING4 0
+#endif
 template <typename T, int BLK, int HD>
 constexpr int dq_groups() {
   return std::is_same<T, bf16_t>::value && BLK == 128 && HD == 128 ? GSA_DQ_GROUPS_WIDE : 1;
@@ -315,7 +322,9 @@ struct DqPolicy {
   using S = AttnShape<T, BLK, HD, R, KC>;
   using Item = WorkItem;
   static constexpr int kSub = BLK / KC;                  // pieces per kv-block
-  static constexpr int kLdsBytes = 3 * S::kTileBytes;   // the ring: K, V and a spare
+  static constexpr bool kRing4 = BLK == 128 ? GSA_DQ_RING4_WIDE : GSA_DQ_RING4;
+  // The ring: K, V and a spare (or K and V of this piece and of the next).
+  static constexpr int kLdsBytes = (kRing4 ? 4 : 3) * S::kTileBytes;
 
   const T *q, *k, *v, *o, *dout;
   const float *lse;
@@ -375,8 +384,10 @@ struct DqPolicy {
   // query of group rg): S^T from K and dP^T - D from V.
   f32x4 dsr[R][S::kKB];
   __device__ void compute_a(const Item &it, int e, int piece, int k_slot, int v_slot) {
-    const unsigned char *lk = lds + k_slot * S::kTileBytes;
-    const unsigned char *lv = lds + v_slot * S::kTileBytes;
+    compute_a_at(lds + k_slot * S::kTileBytes, lds + v_slot * S::kTileBytes, it, e, piece);
+  }
+  __device__ __forceinline__ void compute_a_at(const unsigned char *lk, const unsigned char *lv, const Item &it, int e,
+                                               int piece) {
     const bool diag = e == it.end - 1;   // row i ends with its own block j = i
     if constexpr (R == 1) {
 #pragma unroll
@@ -418,6 +429,19 @@ struct DqPolicy {
                                          const Item &it, int e, int piece, bool more, int j_next, int h_next) {
     if (more) S::copy_tile_buf(wr, rv, (uint32_t)((j_next * BLK + h_next * KC) * S::kRowBytes), wave, lane);
     compute_b_at(rd, it, e, piece);
+  }
+  // One step of the four-slot ring: the next piece's K and V into `wk`, `wv` (when `more`),
+  // then this piece from `lk`, `lv`; no two of the four tiles overlap.
+  __device__ __forceinline__ void step4(unsigned char *__restrict__ wk, unsigned char *__restrict__ wv,
+                                        const unsigned char *__restrict__ lk, const unsigned char *__restrict__ lv,
+                                        const Item &it, int e, int piece, bool more, int j_next, int h_next) {
+    if (more) {
+      const uint32_t off = (uint32_t)((j_next * BLK + h_next * KC) * S::kRowBytes);
+      S::copy_tile_buf(wk, rk, off, wave, lane);
+      S::copy_tile_buf(wv, rv, off, wave, lane);
+    }
+    compute_a_at(lk, lv, it, e, piece);
+    compute_b_at(lk, it, e, piece);
   }
   __device__ __forceinline__ void compute_b_at(const unsigned char *lk, const Item &, int, int) {
 #pragma unroll
@@ -464,7 +488,11 @@ __global__ __launch_bounds__(BLK / (16 * dq_groups<T, BLK, HD>()) * 64, HD <= 64
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
   pol.q_in_blk = (threadIdx.x >> 6) * 16 * R + pol.c;
-  run_item_ring(pol, it);
+  if constexpr (P::kRing4) {
+    run_item_ring4(pol, it);
+  } else {
+    run_item_ring(pol, it);
+  }
 }
 
 template <typename T, int BLK, int HD>

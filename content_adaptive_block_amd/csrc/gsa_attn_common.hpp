@@ -464,4 +464,47 @@ __device__ __forceinline__ void run_item_ring(P &pol, const WorkItem &it) {
   pol.finish(it);
 }
 
+// ---------------------------------------------------------------------------------------
+// Four-slot pipeline: K and V of the current piece in one pair of slots, the next piece's
+// K and V copied into the other pair as the step starts.  One barrier per step (after it,
+// every wave has left the previous step, so the other pair is free), and each copy has a
+// whole step to land.  The policy supplies operands/begin/finish, kSub, copy_k, copy_v and
+// step4(write K, write V, read K, read V, item, e, piece, more, j_next, piece_next).
+// ---------------------------------------------------------------------------------------
+template <class P>
+__device__ __forceinline__ void run_item_ring4(P &pol, const WorkItem &it) {
+  constexpr int kSub = P::kSub;
+  constexpr int kTile = P::S::kTileBytes;
+  const int lane = threadIdx.x & (kWave - 1);
+  int chunk = it.beg + 1 + lane < it.end ? it.list[it.beg + 1 + lane] : 0;
+  pol.operands(it);
+  pol.copy_k(it, it.first, 0, 0);
+  pol.copy_v(it, it.first, 0, 1);
+  pol.begin(it);
+  int cur = 0, j = it.first;
+  for (int e = it.beg; e < it.end; ++e) {
+    const int nx_pos = e - it.beg;   // entry e + 1 sits at this position of the chunk run
+#pragma unroll
+    for (int h = 0; h < kSub; ++h) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wg_barrier();
+      const bool last_piece = h + 1 == kSub;
+      const bool more = !last_piece || e + 1 < it.end;
+      int j_next = j;
+      if (last_piece && e + 1 < it.end) {
+        if (nx_pos > 0 && (nx_pos & (kWave - 1)) == 0)
+          chunk = e + 1 + lane < it.end ? it.list[e + 1 + lane] : 0;
+        j_next = __builtin_amdgcn_readlane(chunk, nx_pos & (kWave - 1));
+      }
+      const int h_next = last_piece ? 0 : h + 1;
+      unsigned char *next = pol.lds + (2 - 2 * cur) * kTile;
+      const unsigned char *now = pol.lds + 2 * cur * kTile;
+      pol.step4(next, next + kTile, now, now + kTile, it, e, h, more, j_next, h_next);
+      cur ^= 1;
+      j = j_next;
+    }
+  }
+  pol.finish(it);
+}
+
 }  // namespace gsa

@@ -51,6 +51,16 @@ constexpr float kMaskedScore = -1.0e30f;
 #ifndef GSA_FWD_GROUPS_WIDE
 #define GSA_FWD_GROUPS_WIDE 2
 #endif
+// Four LDS slots (K and V of this piece and of the next, one barrier per step) at b = 128,
+// where registers, not LDS, limit the kernel to two workgroups per CU: 2.05-2.06 vs
+// 2.19-2.20 ms at 2 x 64 KiB (fewer registers too, 201 vs 222).  At b = 64
+// (GSA_FWD_RING4) the three-slot ring keeps six workgroups per CU instead of five.
+#ifndef GSA_FWD_RING4_WIDE
+#define GSA_FWD_RING4_WIDE 1
+#endif
+#ifndef GSA_FWD_RING4
+#define GSA_FWD_RING4 0
+#endif
 template <typename T, int BLK, int HD>
 constexpr int fwd_groups() {
   if (std::is_same<T, bf16_t>::value && HD <= 64 && BLK % 32 == 0) return GSA_FWD_GROUPS;
@@ -64,7 +74,8 @@ struct FwdPolicy {
   using S = AttnShape<T, BLK, HD, R, KC>;
   using Item = WorkItem;
   static constexpr int kSub = BLK / KC;   // pieces per kv-block
-  static constexpr int kLdsBytes = 3 * S::kTileBytes;
+  static constexpr bool kRing4 = BLK == 128 ? GSA_FWD_RING4_WIDE : GSA_FWD_RING4;
+  static constexpr int kLdsBytes = (kRing4 ? 4 : 3) * S::kTileBytes;
 
   const T *q, *k, *v;
   T *o;
@@ -107,7 +118,10 @@ struct FwdPolicy {
   // S^T tiles: lane holds keys piece*KC + kb*16 + 4g + rr of query q0 + 16 r.
   f32x4 st[R][S::kKB];
   __device__ void compute_a(const Item &it, int e, int piece, int k_slot, int) {
-    const unsigned char *lk = lds + k_slot * S::kTileBytes;
+    compute_a_at(lds + k_slot * S::kTileBytes, nullptr, it, e, piece);
+  }
+  __device__ __forceinline__ void compute_a_at(const unsigned char *lk, const unsigned char *, const Item &it, int e,
+                                               int piece) {
 #pragma unroll
     for (int kb = 0; kb < S::kKB; ++kb) {
       f32x4 t[R];
@@ -157,6 +171,19 @@ struct FwdPolicy {
     if (more) S::copy_tile_buf(wr, rv, (uint32_t)((j_next * BLK + h_next * KC) * S::kRowBytes), wave, lane);
     compute_b_at(rd, it, e, piece);
   }
+  // One step of the four-slot ring: the next piece's K and V into `wk`, `wv` (when `more`),
+  // then this piece from `lk`, `lv`; no two of the four tiles overlap.
+  __device__ __forceinline__ void step4(unsigned char *__restrict__ wk, unsigned char *__restrict__ wv,
+                                        const unsigned char *__restrict__ lk, const unsigned char *__restrict__ lv,
+                                        const Item &it, int e, int piece, bool more, int j_next, int h_next) {
+    if (more) {
+      const uint32_t off = (uint32_t)((j_next * BLK + h_next * KC) * S::kRowBytes);
+      S::copy_tile_buf(wk, rk, off, wave, lane);
+      S::copy_tile_buf(wv, rv, off, wave, lane);
+    }
+    compute_a_at(lk, lv, it, e, piece);
+    compute_b_at(lv, it, e, piece);
+  }
   __device__ __forceinline__ void compute_b_at(const unsigned char *lv, const Item &, int, int) {
 #pragma unroll
     for (int part = 0; part < S::kParts; ++part)
@@ -204,7 +231,11 @@ __global__ __launch_bounds__((BLK / (16 * fwd_groups<T, BLK, HD>()) * 64),
   pol.c = threadIdx.x & 15;
   pol.g = (threadIdx.x & 63) >> 4;
   pol.q0 = (threadIdx.x >> 6) * 16 * R + pol.c;
-  run_item_ring(pol, it);
+  if constexpr (P::kRing4) {
+    run_item_ring4(pol, it);
+  } else {
+    run_item_ring(pol, it);
+  }
 }
 
 template <typename T, int BLK, int HD>
