@@ -13,13 +13,15 @@ text-like bytes (the pages' PG-19 runs at 8K bytes are the shape it stands in fo
 
 Timing: the primary figures are cold-cache steps.  Before each step a 512 MiB buffer
 (larger than the 256 MB Infinity Cache) is read, outside the events that time the step,
-so that no line of the workload's tensors is cached when it starts; HIP events on the
-launch stream mark the step's start and the end of every kernel.  The flush reads
+so that no line of the workload's tensors is cached when it starts.  The flush reads
 rather than writes: a written buffer leaves the Infinity Cache full of dirty lines, and
 the step's first kernel then pays for writing them back to HBM (``cold_write_fill``
-reports the step time under that protocol).  The device first runs ``--settle-ms`` of such steps untimed (its clocks settle
-under sustained load), then ``--warmup`` steps, then ``--steps`` timed steps; the step
-time is their median.  ``warm`` gives the same for back-to-back steps with nothing in
+reports the step time under that protocol).  HIP events on the launch stream mark each
+timed step's start and end; the per-kernel times come from as many more cold steps with
+an event after every kernel (each such event holds the next kernel back by about 5 us).
+The device first runs ``--settle-ms`` of such steps untimed (its clocks settle under
+sustained load), then ``--warmup`` steps, then ``--steps`` timed steps; the step time is
+their median.  ``warm`` gives the same for back-to-back steps with nothing in
 between (secondary).
 
 Prints ONE JSON line.  ``value`` is effective TFLOP/s on kept blocks: algorithmic
@@ -413,13 +415,24 @@ class DevicePath:
             flush()
             self.step()
         torch.cuda.synchronize()
+        # Step times: events only at each step's start and end.  An event recorded between
+        # two kernels holds the next one back by about 5 us of queue time, which is no part
+        # of the step's work.
+        marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for k in range(steps):
+            flush()
+            marks[k][0].record(self.stream)
+            self.step()
+            marks[k][1].record(self.stream)
+        torch.cuda.synchronize()
+        step_ms = [a.elapsed_time(b) for a, b in marks]
+        # Per-kernel times: as many more cold steps, with an event after every kernel.
         evs = [self.events() for _ in range(steps)]
         for k in range(steps):
             flush()
             self.step(evs[k])
         torch.cuda.synchronize()
         per = {nm: [ev[i].elapsed_time(ev[i + 1]) for ev in evs] for i, nm in enumerate(self.kernels)}
-        step_ms = [ev[0].elapsed_time(ev[-1]) for ev in evs]
         return (float(np.median(step_ms)), float(np.mean(step_ms)), {nm: float(np.mean(v)) for nm, v in per.items()},
                 step_ms)
 
