@@ -341,9 +341,11 @@ struct DqPolicy {
   float lse2[R], dd[R];
   f32x4 acc[R][S::kDB];
 
-  __device__ void operands(const Item &it) {
+  __device__ void resources(const Item &it) {
     rk = make_rsrc(k + it.sh * seq * HD, (uint32_t)(seq * S::kRowBytes));
     rv = make_rsrc(v + it.sh * seq * HD, (uint32_t)(seq * S::kRowBytes));
+  }
+  __device__ void operands(const Item &it) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk + 16 * r;

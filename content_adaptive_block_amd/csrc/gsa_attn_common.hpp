@@ -412,8 +412,9 @@ __device__ __forceinline__ void run_item3(P &pol, const WorkItem &it) {
 //   free); copy the next piece's K into the spare slot; compute_a (reads K, and V if it
 //   wants); barrier (everyone is done with the slot the policy frees: K when kFreeK, else
 //   V); step_b: copy the next piece's V into it and compute the second half.
-// The policy supplies operands/begin/finish as for run_item, plus the constants kSub and
-// kFreeK, copy_k(item, j, piece, slot), copy_v(item, j, piece, slot),
+// The policy supplies operands/begin/finish as for run_item, resources(item) (the buffer
+// resources the copies need, set before operands), the constants kSub and kFreeK,
+// copy_k(item, j, piece, slot), copy_v(item, j, piece, slot),
 // compute_a(item, e, piece, k_slot, v_slot) and step_b(write, read, item, e, piece, more,
 // j_next, piece_next), which copies the next piece's V (when `more`) to `write` and computes
 // from the tile at `read` (V when kFreeK, else K).  The two pointers are restrict: the
@@ -425,10 +426,13 @@ __device__ __forceinline__ void run_item_ring(P &pol, const WorkItem &it) {
   constexpr int kSub = P::kSub;
   const int lane = threadIdx.x & (kWave - 1);
   int chunk = it.beg + 1 + lane < it.end ? it.list[it.beg + 1 + lane] : 0;
-  pol.operands(it);
+  // The first tiles' copies go out before the register operands are loaded (dQ forms D
+  // from its rows right away, and would otherwise hold the copies back until they land).
+  pol.resources(it);
   int ks = 0, vs = 1, spare = 2;
   pol.copy_k(it, it.first, 0, ks);
   pol.copy_v(it, it.first, 0, vs);
+  pol.operands(it);
   pol.begin(it);
   int j = it.first;
   for (int e = it.beg; e < it.end; ++e) {
@@ -477,9 +481,10 @@ __device__ __forceinline__ void run_item_ring4(P &pol, const WorkItem &it) {
   constexpr int kTile = P::S::kTileBytes;
   const int lane = threadIdx.x & (kWave - 1);
   int chunk = it.beg + 1 + lane < it.end ? it.list[it.beg + 1 + lane] : 0;
-  pol.operands(it);
+  pol.resources(it);   // as in run_item_ring: the first copies go out first
   pol.copy_k(it, it.first, 0, 0);
   pol.copy_v(it, it.first, 0, 1);
+  pol.operands(it);
   pol.begin(it);
   int cur = 0, j = it.first;
   for (int e = it.beg; e < it.end; ++e) {

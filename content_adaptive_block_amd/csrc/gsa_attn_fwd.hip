@@ -91,10 +91,12 @@ struct FwdPolicy {
   f32x4 acc[R][S::kDB];
   float m_run[R], l_part[R];
 
-  __device__ void operands(const Item &it) {
+  __device__ void resources(const Item &it) {
     const int64_t slice = seq * HD;
     rk = make_rsrc(k + it.sh * slice, (uint32_t)(slice * sizeof(T)));
     rv = make_rsrc(v + it.sh * slice, (uint32_t)(slice * sizeof(T)));
+  }
+  __device__ void operands(const Item &it) {
     const int64_t row0 = it.sh * seq + (int64_t)it.blk * BLK + q0;
 #pragma unroll
     for (int r = 0; r < R; ++r) S::load_row_frag(qf[r], q + (row0 + 16 * r) * HD, g);
