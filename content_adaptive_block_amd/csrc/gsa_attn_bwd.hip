@@ -241,18 +241,14 @@ struct DkdvPolicy {
       S::template accumulate_part_n<R>(&dk_acc[0][0], lq, &ds[0][0], S::kPartTiles, part, c, g);
     }
   }
-  __device__ void finish(const Item &it) {
-    // Lane holds features db*16 + 4g + r of its key: four consecutive features.
+  __device__ void finish(const Item &it, unsigned char *area) {
+    static_assert(S::kWaves * S::kAreaBytes <= kStageBytes, "output staging fits a free stage");
+    unsigned char *own = area + wave * S::kAreaBytes;
 #pragma unroll
     for (int kg = 0; kg < R; ++kg) {
-      const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key0 + 16 * kg;
-      T *dkr = dk + key_row * HD;
-      T *dvr = dv + key_row * HD;
-#pragma unroll
-      for (int db = 0; db < S::kDB; ++db) {
-        S::store4(dkr + db * 16 + 4 * g, dk_acc[kg][db] * -scale);   // the sum holds -dK / scale
-        S::store4(dvr + db * 16 + 4 * g, dv_acc[kg][db]);
-      }
+      const int64_t key_row = it.sh * seq + (int64_t)it.blk * BLK + key0 + 16 * kg;   // this lane's key
+      S::store_rows(dk + key_row * HD, dk_acc[kg], -scale, own, c, g, lane);   // the sum holds -dK / scale
+      S::store_rows(dv + key_row * HD, dv_acc[kg], 1.0f, own, c, g, lane);
     }
   }
 };
@@ -325,6 +321,7 @@ struct DqPolicy {
   static constexpr bool kRing4 = BLK == 128 ? GSA_DQ_RING4_WIDE : GSA_DQ_RING4;
   // The ring: K, V and a spare (or K and V of this piece and of the next).
   static constexpr int kLdsBytes = (kRing4 ? 4 : 3) * S::kTileBytes;
+  static_assert(S::kWaves * S::kAreaBytes <= (kRing4 ? 2 : 1) * S::kTileBytes, "output staging fits the free slots");
 
   const T *q, *k, *v, *o, *dout;
   const float *lse;
@@ -450,13 +447,11 @@ struct DqPolicy {
     for (int part = 0; part < S::kParts; ++part)
       S::template accumulate_part_n<R>(&acc[0][0], lk, &dsr[0][part * S::kPartTiles], S::kKB, part, c, g);
   }
-  __device__ void finish(const Item &it) {
+  __device__ void finish(const Item &it, unsigned char *area) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk + 16 * r;
-      T *dqr = dq + q_row * HD;
-#pragma unroll
-      for (int db = 0; db < S::kDB; ++db) S::store4(dqr + db * 16 + 4 * g, acc[r][db] * scale);
+      const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q_in_blk + 16 * r;   // this lane's row
+      S::store_rows(dq + q_row * HD, acc[r], scale, area + wave * S::kAreaBytes, c, g, lane);
     }
   }
 };

@@ -102,6 +102,13 @@ constexpr int kv_piece_rows() {
   return std::is_same<T, bf16_t>::value && BLK == 128 && HD == 128 ? GSA_PIECE_ROWS_128 : BLK;
 }
 
+// Outputs (O, dQ, dK, dV) leave through LDS in whole rows (AttnShape::store_rows): at
+// 8 x 8 KiB the step took 0.394-0.396 vs 0.425-0.428 ms (forward 98 vs 106 us, dQ 140 vs
+// 146, dK/dV 148 vs 166); at 2 x 64 KiB neutral to 2% faster.
+#ifndef GSA_STORE_VIA_LDS
+#define GSA_STORE_VIA_LDS 1
+#endif
+
 // R = 16-row groups owned by each wave (1 or 2); the workgroup has BLK / (16 R) waves.
 // KC = rows of a staged tile: the whole block (BLK), or a part of it when the other side
 // streams each block in KC-row pieces.
@@ -292,6 +299,39 @@ struct AttnShape {
     for (int part = 0; part < kParts; ++part) accumulate_part(acc, lds, cm + part * kPartTiles, part, c, g);
   }
 
+  // Stores the 16 rows of one row group (row c of the group in lane c) whose HD features a
+  // wave holds in the C layout (acc[db][r] = feature db*16 + 4g + r), times `mul`; `mine` is
+  // this lane's row, and the group's rows are consecutive in memory.  With kStoreViaLds (bf16) the rows pass through
+  // the wave's own 16-row area of LDS at `area`, so that each store instruction writes 64
+  // lanes x 16 contiguous bytes instead of sixteen 32-byte pieces of rows.  Only this wave
+  // touches `area`, and a wave's LDS accesses complete in order, so no barrier is needed.
+  static constexpr bool kStoreViaLds = kBf16 && GSA_STORE_VIA_LDS;
+  static constexpr int kAreaBytes = 16 * kRowBytes;   // LDS per wave for store_rows
+  __device__ static __forceinline__ void store_rows(T *mine, const f32x4 *acc, float mul, unsigned char *area, int c,
+                                                    int g, int lane) {
+    if constexpr (!kStoreViaLds) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) store4(mine + db * 16 + 4 * g, acc[db] * mul);
+    } else {
+      T *dst = mine - c * HD;   // the group's first row
+      // Row c's 16-byte chunks sit at chunk ^ (c & 7), which spreads the sixteen rows that one
+      // write instruction touches over the banks.
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const f32x4 x = acc[db] * mul;
+        const bf16x4 y = {to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
+        const int ch = 2 * db + (g >> 1);
+        *reinterpret_cast<bf16x4 *>(area + c * kRowBytes + ((ch ^ (c & 7)) << 4) + (g & 1) * 8) = y;
+      }
+#pragma unroll
+      for (int it = 0; it < 16 * kChunks / 64; ++it) {
+        const int kx = it * 64 + lane, row = kx / kChunks, ch = kx % kChunks;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(area + row * kRowBytes + ((ch ^ (row & 7)) << 4));
+        *reinterpret_cast<u32x4 *>(dst + row * HD + ch * kVec) = val;
+      }
+    }
+  }
+
   // Stores four consecutive features.
   __device__ static __forceinline__ void store4(T *dst, const f32x4 &x) {
     if constexpr (kBf16) {
@@ -315,7 +355,8 @@ struct AttnShape {
 //                                    copy piece `copy_piece` of `block` to the stage at
 //                                    `write` (when do_copy), then compute piece `piece` of
 //                                    list entry e from the stage at `read`
-//   finish(item)                     write the item's outputs
+//   finish(item, area)               write the item's outputs (`area`: LDS free of reads
+//                                    and copies, for store_rows)
 // A step waits for its own copies, synchronises -- after which every wave has finished
 // the previous step, so the other stage is free -- issues the next piece's copies and
 // computes.  The two stage pointers are restrict, so that the compiler does not make the
@@ -354,7 +395,7 @@ __device__ __forceinline__ void run_item(P &pol, const WorkItem &it) {
       stage ^= 1;
     }
   }
-  pol.finish(it);
+  pol.finish(it, pol.lds + stage * P::kStageBytes);   // no copy went there in the last step
 }
 
 
@@ -399,7 +440,7 @@ __device__ __forceinline__ void run_item3(P &pol, const WorkItem &it) {
       stage = stage == 2 ? 0 : stage + 1;
     }
   }
-  pol.finish(it);
+  pol.finish(it, pol.lds + stage * P::kStageBytes);   // neither read nor written in the last step
 }
 
 // ---------------------------------------------------------------------------------------
@@ -465,7 +506,7 @@ __device__ __forceinline__ void run_item_ring(P &pol, const WorkItem &it) {
       j = j_next;
     }
   }
-  pol.finish(it);
+  pol.finish(it, pol.lds + ks * P::S::kTileBytes);   // the last step's spare slot: untouched
 }
 
 // ---------------------------------------------------------------------------------------
@@ -509,7 +550,7 @@ __device__ __forceinline__ void run_item_ring4(P &pol, const WorkItem &it) {
       j = j_next;
     }
   }
-  pol.finish(it);
+  pol.finish(it, pol.lds + 2 * cur * kTile);   // the pair no copy went to in the last step
 }
 
 }  // namespace gsa

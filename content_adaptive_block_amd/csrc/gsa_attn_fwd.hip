@@ -76,6 +76,7 @@ struct FwdPolicy {
   static constexpr int kSub = BLK / KC;   // pieces per kv-block
   static constexpr bool kRing4 = BLK == 128 ? GSA_FWD_RING4_WIDE : GSA_FWD_RING4;
   static constexpr int kLdsBytes = (kRing4 ? 4 : 3) * S::kTileBytes;
+  static_assert(S::kWaves * S::kAreaBytes <= (kRing4 ? 2 : 1) * S::kTileBytes, "output staging fits the free slots");
 
   const T *q, *k, *v;
   T *o;
@@ -191,15 +192,13 @@ struct FwdPolicy {
     for (int part = 0; part < S::kParts; ++part)
       S::template accumulate_part_n<R>(&acc[0][0], lv, &st[0][part * S::kPartTiles], S::kKB, part, c, g);
   }
-  __device__ void finish(const Item &it) {
+  __device__ void finish(const Item &it, unsigned char *area) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float l = group_sum4(l_part[r]);
       const float inv = 1.0f / l;
-      const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q0 + 16 * r;
-      T *orow = o + q_row * HD;
-#pragma unroll
-      for (int db = 0; db < S::kDB; ++db) S::store4(orow + db * 16 + 4 * g, acc[r][db] * inv);
+      const int64_t q_row = it.sh * seq + (int64_t)it.blk * BLK + q0 + 16 * r;   // this lane's row
+      S::store_rows(o + q_row * HD, acc[r], inv, area + wave * S::kAreaBytes, c, g, lane);
       if (lse != nullptr && g == 0) lse[q_row] = (m_run[r] + __log2f(l)) * 0.69314718055994531f;
     }
   }
