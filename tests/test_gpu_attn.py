@@ -158,6 +158,42 @@ def test_row0_is_v0_and_determinism(inst):
         assert torch.equal(r1[nm], r2[nm]), nm
 
 
+@pytest.mark.parametrize("inst", [("bf16", 64, 64), ("bf16", 128, 128)])
+def test_running_max_raised_and_kept(inst):
+    """The forward's online softmax when scores move a lot between the kv-blocks of a row.
+
+    Three local heads with a window over the whole prefix, so row i visits blocks 0..i in
+    ascending order.  Head 0: every block's scores exceed the previous block's by about 10
+    in exp2 units, more than the 2^8 slack, so the running max is raised (and O and l
+    rescaled) at every entry while O already holds earlier blocks.  Head 1: the scores fall
+    by as much, so the first block sets the max for good and later blocks underflow to
+    nearly nothing.  Head 2: ordinary random inputs.  Random inputs never exercise the
+    raise after the first block."""
+    dtype, block, hd = inst
+    n, n_heads = 8, (3, 0, 0)
+    log(f"  running max {dtype} b={block} d={hd} N={n}")
+    x, _ = _inputs(inst, 1, n, 3)
+    t_len = n * block
+    rng = np.random.default_rng(2024)
+    j = (np.arange(t_len) // block).astype(np.float64)[:, None]
+    step = 10.0 / (np.log2(np.e) * np.sqrt(hd))   # q.k * scale * log2(e) grows 10 per block
+    q = 1.0 + 0.05 * rng.standard_normal((1, 3, t_len, hd))
+    k = 0.05 * rng.standard_normal((1, 3, t_len, hd))
+    k[0, 0] += step * j
+    k[0, 1] += step * (n - 1 - j)
+    q[0, 2] = 0.125 * rng.standard_normal((t_len, hd))
+    k[0, 2] = 0.125 * rng.standard_normal((t_len, hd))
+    v = 0.25 * rng.standard_normal((1, 3, t_len, hd))
+    t = {nm: torch.from_numpy(a).to(torch.bfloat16) for nm, a in (("q", q), ("k", k), ("v", v))}
+    res = run_path(x, block, n - 1, n_heads, t, backward=False)
+    masks = check_mask(res["mask"], res["c"], block, n - 1, n_heads)
+    ref_o, ref_lse = oracle.attn_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), masks, n_heads, block)
+    # the scores really do climb past the slack: the last block's reference sits far above the first's
+    assert float(ref_lse[0, 0, -1] - ref_lse[0, 0, block - 1]) * np.log2(np.e) > 8 * (n - 1)
+    assert_close("O", f64(res["o"]), ref_o, BF16_TOL)
+    assert_close("LSE", f64(res["lse"]), ref_lse, 1e-3)
+
+
 def test_locality_outside_kept_blocks():
     inst = ("bf16", 64, 64)
     n_heads, window, block = (1, 1, 1), 1, 64
