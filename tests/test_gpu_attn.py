@@ -168,7 +168,8 @@ def test_running_max_raised_and_kept(inst):
     rescaled) at every entry while O already holds earlier blocks.  Head 1: the scores fall
     by as much, so the first block sets the max for good and later blocks underflow to
     nearly nothing.  Head 2: ordinary random inputs.  Random inputs never exercise the
-    raise after the first block."""
+    raise after the first block.  The backward takes these rows' large LSE (about 53) back
+    out of every exponential."""
     dtype, block, hd = inst
     n, n_heads = 8, (3, 0, 0)
     log(f"  running max {dtype} b={block} d={hd} N={n}")
@@ -184,14 +185,18 @@ def test_running_max_raised_and_kept(inst):
     q[0, 2] = 0.125 * rng.standard_normal((t_len, hd))
     k[0, 2] = 0.125 * rng.standard_normal((t_len, hd))
     v = 0.25 * rng.standard_normal((1, 3, t_len, hd))
-    t = {nm: torch.from_numpy(a).to(torch.bfloat16) for nm, a in (("q", q), ("k", k), ("v", v))}
-    res = run_path(x, block, n - 1, n_heads, t, backward=False)
+    do = rng.standard_normal((1, 3, t_len, hd))
+    t = {nm: torch.from_numpy(a).to(torch.bfloat16) for nm, a in (("q", q), ("k", k), ("v", v), ("do", do))}
+    res = run_path(x, block, n - 1, n_heads, t, backward=True)
     masks = check_mask(res["mask"], res["c"], block, n - 1, n_heads)
     ref_o, ref_lse = oracle.attn_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), masks, n_heads, block)
     # the scores really do climb past the slack: the last block's reference sits far above the first's
     assert float(ref_lse[0, 0, -1] - ref_lse[0, 0, block - 1]) * np.log2(np.e) > 8 * (n - 1)
     assert_close("O", f64(res["o"]), ref_o, BF16_TOL)
     assert_close("LSE", f64(res["lse"]), ref_lse, 1e-3)
+    ref_g = oracle.attn_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), masks, n_heads, block)
+    for nm, ref in zip(("dq", "dk", "dv"), ref_g):
+        assert_close(nm, f64(res[nm]), ref, BF16_TOL)
 
 
 def test_locality_outside_kept_blocks():
