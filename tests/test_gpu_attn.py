@@ -14,7 +14,7 @@ import torch
 import content_adaptive_block_amd as gsa
 import oracle
 import synth
-from gpu_cases import BF16_TOL, F32_TOL, assert_close, check_mask, f64, log, oracle_map, run_path
+from gpu_cases import BF16_TOL, F32_TOL, assert_close, check_mask, f64, log, max_err, oracle_map, run_path
 
 pytestmark = pytest.mark.gpu
 
@@ -197,6 +197,37 @@ def test_running_max_raised_and_kept(inst):
     ref_g = oracle.attn_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), masks, n_heads, block)
     for nm, ref in zip(("dq", "dk", "dv"), ref_g):
         assert_close(nm, f64(res[nm]), ref, BF16_TOL)
+
+
+@pytest.mark.parametrize("inst,scale", [(("f32", 16, 32), 0.5), (("bf16", 64, 64), 0.05),
+                                        (("bf16", 128, 128), 0.02)])
+def test_explicit_softmax_scale(inst, scale):
+    """A softmax scale given by the caller instead of 1/sqrt(d), forward and backward."""
+    dtype, block, hd = inst
+    batch, n, n_heads, window = 2, 5, (1, 1, 1), 1
+    log(f"  scale {scale}: {dtype} b={block} d={hd} B={batch} N={n}")
+    x, t = _inputs(inst, batch, n, sum(n_heads))
+    c = gsa.gsa_prepare(x, block)
+    m = gsa.gsa_build_mask(torch.from_numpy(c).cuda(), window, n_heads)
+    q, k, v, do = (t[nm].cuda() for nm in ("q", "k", "v", "do"))
+    o, lse = gsa.gsa_attn_fwd(q, k, v, m, block, scale=scale)
+    dq, dk, dv = gsa.gsa_attn_bwd(q, k, v, o, lse, do, m, block, scale=scale)
+    torch.cuda.synchronize()
+    masks = check_mask(m, c, block, window, n_heads)
+    ref_o, ref_lse = oracle.attn_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), masks, n_heads, block, scale=scale)
+    ref_g = oracle.attn_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), masks, n_heads, block,
+                            scale=scale)
+    tol, ltol = _tol(dtype)
+    assert_close("O", f64(o), ref_o, tol)
+    assert_close("LSE", f64(lse), ref_lse, ltol)
+    for nm, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), ref_g):
+        assert_close(nm, f64(got), ref, tol)
+        # small scales make dQ and dK small: also bound the error relative to their size
+        assert max_err(f64(got), ref) <= 0.02 * float(np.max(np.abs(ref))), nm
+    # the default differs from this scale, so the scale really reached the kernels
+    o_def = gsa.gsa_attn_fwd(q, k, v, m, block, with_lse=False)
+    torch.cuda.synchronize()
+    assert not torch.equal(o_def, o)
 
 
 def test_locality_outside_kept_blocks():
