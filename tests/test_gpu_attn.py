@@ -224,10 +224,13 @@ def test_explicit_softmax_scale(inst, scale):
         assert_close(nm, f64(got), ref, tol)
         # small scales make dQ and dK small: also bound the error relative to their size
         assert max_err(f64(got), ref) <= 0.02 * float(np.max(np.abs(ref))), nm
-    # the default differs from this scale, so the scale really reached the kernels
+    # the default differs from this scale, so the scale really reached the kernels; and
+    # a forward without LSE output gives the same O as one with it
     o_def = gsa.gsa_attn_fwd(q, k, v, m, block, with_lse=False)
+    o_def2, _ = gsa.gsa_attn_fwd(q, k, v, m, block)
     torch.cuda.synchronize()
     assert not torch.equal(o_def, o)
+    assert torch.equal(o_def, o_def2)
 
 
 def test_locality_outside_kept_blocks():
