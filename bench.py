@@ -619,7 +619,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(samples shard across GPUs with no communication; run --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
