@@ -351,6 +351,47 @@ def test_full_size_sampled(cid):
     _compare_sampled(errs, ltol, tol)
 
 
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_full_batch_every_output(cid):
+    """Every output element of the whole batch at full size against the oracle (the
+    8 x 4 KiB and 8 x 8 KiB workloads; the oracle takes about a second per (sample, head)
+    for the backward, so the 2 x 64 KiB workload stays sampled above)."""
+    wl = synth.WORKLOADS[cid]
+    block = wl.block
+    names = ("q", "k", "v", "do") if wl.backward else ("q", "k", "v")
+    log(f"  cfg{cid} whole batch: B={wl.batch} T={wl.seq_len} H={wl.heads} bwd={wl.backward}")
+    x = synth.gen_bytes(wl)
+    t = synth.gen_tensors(wl, names)
+    res = run_path(x, block, wl.window, wl.n_heads, t, backward=wl.backward)
+    masks = check_mask(res["mask"], res["c"], block, wl.window, wl.n_heads)
+    classes = oracle.head_classes(wl.n_heads)
+    outs = ("o", "lse") + (("dq", "dk", "dv") if wl.backward else ())
+    got = {nm: f64(res[nm]) for nm in outs}
+    host = {nm: f64(t[nm]) for nm in names}
+
+    def pair(s, h):
+        nh = [0, 0, 0]
+        nh[classes[h]] = 1
+        sub = np.zeros((1, 3) + masks.shape[2:], dtype=bool)
+        sub[0, classes[h]] = masks[s, classes[h]]
+        one = {nm: host[nm][s:s + 1, h:h + 1] for nm in names}
+        refs = list(oracle.attn_fwd(one["q"], one["k"], one["v"], sub, tuple(nh), block))
+        if wl.backward:
+            refs += list(oracle.attn_bwd(one["q"], one["k"], one["v"], one["do"], sub, tuple(nh), block))
+        return [r[0, 0] for r in refs]
+
+    jobs = [(s, h) for s in range(wl.batch) for h in range(wl.heads)]
+    ref = {nm: np.empty_like(got[nm]) for nm in outs}
+    for (s, h), refs in zip(jobs, oracle_map(pair, jobs)):
+        for nm, r in zip(outs, refs):
+            ref[nm][s, h] = r
+    tol = BF16_TOL
+    for nm in outs:
+        assert_close(nm, got[nm], ref[nm], 1e-3 if nm == "lse" else tol)
+    for nm in ("dq", "dk") if wl.backward else ():   # of order 0.1 here: also a relative bound
+        assert max_err(got[nm], ref[nm]) <= 0.02 * float(np.max(np.abs(ref[nm]))), nm
+
+
 @pytest.mark.parametrize("inst", list(BASE))
 def test_backward_stage_entry_points(inst):
     """dq then dkdv equals the whole backward bit for bit; dq writes D = rowsum(dO * O);
