@@ -12,17 +12,19 @@
 //   bwd_dkdv  one workgroup per (sample, head, kv-block j), walking the CSC column of j
 //             (query blocks i that keep j); each wave keeps 16 or 32 keys of K_j, V_j in
 //             registers and accumulates dK^T, dV^T tiles in fp32 while Q_i, dO_i, LSE_i
-//             and D_i stream through two LDS stages by asynchronous global -> LDS copies
-//             one piece ahead (32-row pieces at b = 64, whole blocks otherwise); Q_i^T
-//             and dO_i^T come from transposing LDS reads.
+//             and D_i stream through LDS by asynchronous global -> LDS copies: at b = 64
+//             as 32-row pieces on three stages, each copied two pieces ahead; otherwise
+//             as whole blocks on two stages, one ahead.  Q_i^T and dO_i^T come from
+//             transposing LDS reads.
 //   bwd_dq    one workgroup per (sample, head, query block i), walking the CSR row of i;
 //             each wave keeps 16 query rows (32 at b = d = 128) of Q_i and dO_i in
-//             registers and accumulates
-//             dQ^T while K_j and V_j stream through a ring of three LDS slots (V's slot
-//             takes the next V as soon as dS is formed; K^T by transposing reads); at
-//             b = 128, d = 128 the blocks stream as 64-row pieces.
+//             registers and accumulates dQ^T while K_j and V_j stream through a ring of
+//             three LDS slots (V's slot takes the next V as soon as dS is formed; K^T by
+//             transposing reads); at b = d = 128 the blocks stream as 64-row pieces
+//             through four slots (this piece's K and V, and the next piece's).
 //             It also forms D of its rows from O and dO and writes it for dK/dV, so the
 //             full backward runs dQ, then dK/dV, with no separate pass for D.
+// dK, dV and dQ leave through LDS in whole rows (AttnShape::store_rows).
 #include <type_traits>
 
 #include "gsa_attn_common.hpp"

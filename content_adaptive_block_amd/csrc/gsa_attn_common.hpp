@@ -2,13 +2,15 @@
 //
 // A "tile" is one mask block of one head: BLK token rows of HD features, contiguous in
 // memory ([B, H, T, d] layout), i.e. a dense BLK x HD row-major matrix.  Each wave owns
-// 16 rows of its workgroup's own block, kept in registers; the other side's tiles are
-// staged row-major in LDS and read two ways:
-//   dot_rows:      C[m][n] = sum_f LDS[m][f] * F[n][f]    (A = 16 staged rows, b128 reads;
-//                  B = the wave's register fragment F)    -> a C tile whose rows m are
-//                  staged tokens (4 per lane) and whose column n is one of the wave's rows
-//   accumulate_pv: Acc[f][n] += sum_m LDS[m][f] * C[m][n] (A = the staged tile transposed,
-//                  read with ds_read_b64_tr_b16; B = a C tile from dot_rows fed back)
+// 16 rows (one group; 32 with two groups) of its workgroup's own block, kept in
+// registers; the other side's tiles are staged row-major in LDS and read two ways:
+//   dot_rows:        C[m][n] = sum_f LDS[m][f] * F[n][f]    (A = 16 staged rows, b128
+//                    reads; B = the wave's register fragment F) -> a C tile whose rows m
+//                    are staged tokens (4 per lane) and whose column n is one of the
+//                    wave's rows
+//   accumulate_part: Acc[f][n] += sum_m LDS[m][f] * C[m][n] (A = the staged tile
+//                    transposed, read with ds_read_b64_tr_b16; B = C tiles from dot_rows
+//                    fed back)
 // The second product takes a lane's four C rows of two adjacent 16-row tiles as its eight
 // K-slots; the transposed read delivers the other operand in the same token order.
 //
@@ -16,6 +18,10 @@
 // Tiles arrive by asynchronous global -> LDS copies (no register staging).  The
 // swizzle keeps both read forms free of bank conflicts (measured on gfx950: 128-byte rows
 // use (row >> 1) & 7, 256-byte rows ((row & 7) << 1) | ((row >> 3) & 1)).
+//
+// The item pipelines below (run_item, run_item3, run_item_ring, run_item_ring4) drive a
+// kernel's policy through its list, and store_rows writes a wave's outputs through LDS
+// in whole rows.
 //
 // Lane layout of ds_read_b64_tr_b16 (measured on gfx950): within each group of 16 lanes,
 // lane i receives element i % 4 of the 8 bytes addressed by lane 4e + i / 4, for
@@ -292,19 +298,13 @@ struct AttnShape {
     }
   }
 
-  // acc[db] += (staged tile)^T[db*16 + c][tokens] x C, C = kKB tiles of 16 staged tokens.
-  __device__ static __forceinline__ void accumulate_pv(f32x4 *acc, const unsigned char *lds, const f32x4 *cm,
-                                                        int c, int g) {
-#pragma unroll
-    for (int part = 0; part < kParts; ++part) accumulate_part(acc, lds, cm + part * kPartTiles, part, c, g);
-  }
-
   // Stores the 16 rows of one row group (row c of the group in lane c) whose HD features a
-  // wave holds in the C layout (acc[db][r] = feature db*16 + 4g + r), times `mul`; `mine` is
-  // this lane's row, and the group's rows are consecutive in memory.  With kStoreViaLds (bf16) the rows pass through
-  // the wave's own 16-row area of LDS at `area`, so that each store instruction writes 64
-  // lanes x 16 contiguous bytes instead of sixteen 32-byte pieces of rows.  Only this wave
-  // touches `area`, and a wave's LDS accesses complete in order, so no barrier is needed.
+  // wave holds in the C layout (acc[db][r] = feature db*16 + 4g + r), times `mul`; `mine`
+  // is this lane's row, and the group's rows are consecutive in memory.  With
+  // kStoreViaLds (bf16) the rows pass through the wave's own 16-row area of LDS at `area`,
+  // so that each store instruction writes 64 lanes x 16 contiguous bytes instead of
+  // sixteen 32-byte pieces of rows.  Only this wave touches `area`, and a wave's LDS
+  // accesses complete in order, so no barrier is needed.
   static constexpr bool kStoreViaLds = kBf16 && GSA_STORE_VIA_LDS;
   static constexpr int kAreaBytes = 16 * kRowBytes;   // LDS per wave for store_rows
   __device__ static __forceinline__ void store_rows(T *mine, const f32x4 *acc, float mul, unsigned char *area, int c,

@@ -15,10 +15,12 @@
 //     With two 16-row groups per wave every K and V read from LDS feeds two products.
 //   * K_j and V_j stream row-major (swizzled) into a ring of three LDS tiles by
 //     asynchronous global -> LDS copies: K_{j+1} lands in the spare tile while block j
-//     is computed, V_{j+1} in K_j's tile once the scores of block j are done (at
-//     b = 128, d = 128 in 64-row pieces, so that two workgroups fit a CU).  O^T =
-//     V^T P^T reads V^T with transposing LDS loads and takes P straight from the S^T
-//     accumulator (rounded to bf16 in the bf16 instance).
+//     is computed, V_{j+1} in K_j's tile once the scores of block j are done.  At
+//     b = 128, d = 128 they stream in 64-row pieces through four slots (this piece's K
+//     and V, and the next piece's, copied as the step starts), so that two workgroups
+//     fit a CU and a step needs one barrier.  O^T = V^T P^T reads V^T with transposing
+//     LDS loads and takes P straight from the S^T accumulator (rounded to bf16 in the
+//     bf16 instance); O leaves through LDS in whole rows.
 //   * Scores are scaled by scale * log2(e) so every exponential is one exp2.  The
 //     reference max is raised only when a row's max exceeds it by more than 2^8; O and l
 //     share that reference, so the result is unchanged and most rescales are skipped.

@@ -36,8 +36,6 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
-
 // Reduce over the four lane groups that share a column (lanes c, c+16, c+32, c+48).
 // A permlane swap of a value with itself leaves, in its two results, each lane's own
 // value and that of the lane 16 (resp. 32) apart, so one ALU op per step reduces the
