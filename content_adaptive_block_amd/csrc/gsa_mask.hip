@@ -8,10 +8,11 @@
 //   背景与主要改动: heads split into local (M^local U I), literal long-range (M^lit U I)
 //   and their union (hybrid).
 //
-// Kernel 1 (one workgroup of 1024 threads per sample, one thread per block): the sum of
-// c, the flags, literal ranks by wave ballot + popcount prefix, row and column lengths
-// in closed form, one combined exclusive scan into row_ptr/col_ptr, then every list
-// entry is written by its own thread (row found by binary search over the row starts).
+// Kernel 1 (a few 1024-thread workgroups per sample, one thread per block): each forms
+// the sum of c, the flags, literal ranks by wave ballot + popcount prefix, row and column
+// lengths in closed form and one combined exclusive scan into row_ptr/col_ptr (the first
+// workgroup of the sample writes them), then the workgroups share the list entries, each
+// written by its own thread (row found by binary search over the row starts).
 // Row i of each class:
 //   local   : j = max(0, i-w) .. i
 //   literal : literal j <= i if l_i, else i alone

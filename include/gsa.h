@@ -53,7 +53,8 @@ typedef enum { GSA_F32 = 0, GSA_BF16 = 1 } gsa_dtype;
 
 enum { GSA_CLASS_LOCAL = 0, GSA_CLASS_LITERAL = 1, GSA_CLASS_HYBRID = 2, GSA_N_CLASSES = 3 };
 
-/* Largest block count per sample gsa_build_mask accepts (one workgroup per sample). */
+/* Largest block count per sample gsa_build_mask accepts (a sample's flags, ranks and
+ * list starts are formed inside one 1024-thread workgroup). */
 #define GSA_MAX_BLOCKS 1024
 
 /* Short name of a status code; never NULL. */
