@@ -34,9 +34,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{IN
 DEVICE_BASE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-ffast-math", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 DEVICE = DEVICE_BASE + ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
-# The 128 x 128 forward and dQ keep the default, occupancy-first scheduler: with it they
-# fit in 120 VGPRs, so two 8-wave workgroups share a CU (max-ilp needs 132 and keeps one);
-# on 2 x 64 KiB that measured 16% faster.
+# The 128 x 128 forward and dQ keep the default, occupancy-first scheduler.  It was chosen
+# when their waves held one query group (it fit them in 120 VGPRs, two 8-wave workgroups
+# per CU, 16% faster at 2 x 64 KiB than max-ilp's one); with two groups per wave the two
+# schedulers measured within 3% of each other (forward 2.20 vs 2.26 ms, dQ 3.07 vs 3.04).
 DEVICE_WIDE = DEVICE_BASE + ["-DGSA_WIDE_TU"]
 
 

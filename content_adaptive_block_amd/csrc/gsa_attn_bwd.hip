@@ -319,6 +319,8 @@ __global__ __launch_bounds__((BLK / (16 * dkdv_groups<T, BLK, HD>()) * 64),
 #define GSA_DQ_GROUPS_WIDE 2
 #endif
 // Four LDS slots at b = 128 (as for the forward): 2.94-2.96 vs 3.02-3.04 ms at 2 x 64 KiB.
+// At b = 64 (GSA_DQ_RING4) they leave room for five workgroups per CU instead of six:
+// 141.5-141.8 vs 139.3-139.7 us at 8 x 8 KiB.
 #ifndef GSA_DQ_RING4_WIDE
 #define GSA_DQ_RING4_WIDE 1
 #endif

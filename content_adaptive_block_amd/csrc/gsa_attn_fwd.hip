@@ -45,8 +45,8 @@ constexpr float kMaskedScore = -1.0e30f;
 #endif
 // 16-row query groups per wave.  Two groups halve the LDS reads per tile (every K and V
 // read feeds two products) but need more registers.  At b = d = 64 (GSA_FWD_GROUPS) they
-// need 146 VGPRs, which halves the resident waves: 147 vs 135 us at 8 x 8 KiB, so one
-// group.  At b = d = 128 (GSA_FWD_GROUPS_WIDE) eight one-group waves read 512 KiB of LDS
+// need 146 VGPRs, which halves the resident waves at the same six items per CU: 98.2-98.5
+// vs 97.6-98.4 us at 8 x 8 KiB, equal, so one group, with the fewer registers.  At b = d = 128 (GSA_FWD_GROUPS_WIDE) eight one-group waves read 512 KiB of LDS
 // per kept tile, about 90 bytes per clock per CU, so LDS bandwidth binds; two groups (4
 // waves, 215 VGPRs, two waves per SIMD) read half of it: 2.36-2.46 vs 2.56-2.61 ms at
 // 2 x 64 KiB.
@@ -56,7 +56,8 @@ constexpr float kMaskedScore = -1.0e30f;
 // Four LDS slots (K and V of this piece and of the next, one barrier per step) at b = 128,
 // where registers, not LDS, limit the kernel to two workgroups per CU: 2.05-2.06 vs
 // 2.19-2.20 ms at 2 x 64 KiB (fewer registers too, 201 vs 222).  At b = 64
-// (GSA_FWD_RING4) the three-slot ring keeps six workgroups per CU instead of five.
+// (GSA_FWD_RING4) the three-slot ring keeps six workgroups per CU instead of five:
+// 97.6-98.4 vs 102.5-102.9 us at 8 x 8 KiB.
 #ifndef GSA_FWD_RING4_WIDE
 #define GSA_FWD_RING4_WIDE 1
 #endif
